@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the EntmaxKV HIP path on one MI355X.
+
+One step = one decode step for every (sequence, KV head) of the workload:
+refresh of each sequence's tail-page metadata, Gaussian page scoring,
+Gaussian-aware selection, gathered entmax attention (scores, threshold,
+apply).  The headline value is decode tokens/s = batch / median step time,
+with the inputs resident in HBM and the caches flushed (a 512 MiB write)
+between steps, outside the timed events.  Beside it the top-k path and the
+full-cache entmax and split-K softmax baselines are timed the same way.
+
+Each kernel of a step is bracketed by HIP events on the stream the library
+launches on (torch's current stream), which gives the per-kernel durations
+used for the roofline of the dominant kernel.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cluster_1m")
+    ap.add_argument("--seed", type=int, default=3000)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=1,
+                    help="(sequence, KV head) units the oracle is timed on; 0 skips")
+    ap.add_argument("--legs", default="gauss,topk,entmax_full,softmax_full")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU decode step only; this build "
+              "runs on one GPU (got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_entmax_attention_amd as ekv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    spec = workloads.workload(args.workload)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log("[bench] generating %s seed %d" % (spec.name, args.seed))
+    t0 = time.time()
+    inp = workloads.generate(spec, args.seed, dev)
+    torch.cuda.synchronize()
+    log("[bench] inputs ready in %.1fs" % (time.time() - t0))
+    kv = ekv.PagedKV(inp.k, inp.v, inp.page_table, inp.seq_lens, spec.group)
+    buf = ekv.DecodeBuffers(kv, softmax=True)
+    stream = torch.cuda.current_stream()
+    B, H, G, D, P = spec.batch, spec.num_kv_heads, spec.group, spec.head_dim, spec.page_size
+    e = 2 if spec.kv_dtype == "bf16" else 4
+    alpha = spec.alphas[0]
+    k_top = spec.topk or 16
+    delta = spec.delta
+    q = inp.q
+    tail = torch.tensor([(L - 1) // P for L in inp.lens], dtype=torch.int32, device=dev)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    # Full metadata build (once; timed on its own).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    buf.build_meta()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    meta_build_ms = ev0.elapsed_time(ev1)
+
+    # Each leg is a list of (phase name, callable).
+    def ph_meta():
+        buf.build_meta(tail, span_hint=1)
+
+    legs = {
+        "gauss": [
+            ("meta_tail", ph_meta),
+            ("score_gauss", lambda: buf.score(q, ekv.EKV_SCORE_GAUSS)),
+            ("select_gauss", lambda: buf.select_gauss(alpha, delta)),
+            ("entmax_scores", lambda: ekv.ekv_entmax_scores(
+                kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
+            ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
+                kv, alpha, buf.sel, buf.count, buf.tau, buf.ws_decode)),
+            ("entmax_apply", lambda: ekv.ekv_entmax_apply(
+                kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
+        ],
+        "topk": [
+            ("meta_tail", ph_meta),
+            ("score_bbox", lambda: buf.score(q, ekv.EKV_SCORE_BBOX)),
+            ("select_topk", lambda: buf.select_topk(k_top)),
+            ("entmax_scores", lambda: ekv.ekv_entmax_scores(
+                kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
+            ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
+                kv, alpha, buf.sel, buf.count, buf.tau, buf.ws_decode)),
+            ("entmax_apply", lambda: ekv.ekv_entmax_apply(
+                kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
+        ],
+        "entmax_full": [
+            ("entmax_scores", lambda: ekv.ekv_entmax_scores(
+                kv, q, buf.scale, alpha, None, None, buf.ws_decode)),
+            ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
+                kv, alpha, None, None, buf.tau, buf.ws_decode)),
+            ("entmax_apply", lambda: ekv.ekv_entmax_apply(
+                kv, alpha, None, None, buf.out, None, buf.ws_decode)),
+        ],
+        "softmax_full": [
+            ("softmax", lambda: buf.softmax(q)),
+        ],
+    }
+
+    def run_leg(name, steps, warmup):
+        phases = legs[name]
+        for _ in range(warmup):
+            for _, fn in phases:
+                fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+               for _ in range(steps)]
+        t_start = time.perf_counter()
+        for s in range(steps):
+            if flush is not None:
+                flush.fill_(s & 0xFF)
+            evs[s][0].record(stream)
+            for i, (_, fn) in enumerate(phases):
+                fn()
+                evs[s][i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) / steps
+        step_ms = [evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]
+        phase_ms = {pname: statistics.mean(evs[s][i].elapsed_time(evs[s][i + 1])
+                                           for s in range(steps))
+                    for i, (pname, _) in enumerate(phases)}
+        return {"median_ms": statistics.median(step_ms),
+                "p10_ms": float(np.percentile(step_ms, 10)),
+                "p90_ms": float(np.percentile(step_ms, 90)),
+                "wall_ms_incl_flush": wall * 1e3, "phase_ms": phase_ms}
+
+    def selection_stats():
+        cnt = buf.count.cpu().numpy()
+        sel = buf.sel.cpu().numpy()
+        tok = 0
+        for b in range(B):
+            L = inp.lens[b]
+            for h in range(H):
+                pages = sel[b, h, :cnt[b, h]]
+                tok += int(sum(min(P, L - p * P) for p in pages))
+        return int(cnt.sum()), tok
+
+    def support_rows(selected):
+        probs = torch.zeros(B, H * G, inp.max_pages * P, device=dev)
+        buf.entmax(q, alpha, selected=selected, probs=probs)
+        torch.cuda.synchronize()
+        rows = (probs.view(B, H, G, -1) > 0).any(dim=2).sum().item()
+        del probs
+        return int(rows)
+
+    n_pages_total = sum((L + P - 1) // P for L in inp.lens)
+    tokens_total = sum(inp.lens)
+    meta_gauss_bytes = n_pages_total * H * 2 * D * 4
+    meta_bbox_bytes = n_pages_total * H * 2 * D * e
+    tail_bytes = B * H * (P * D * e)
+
+    results = {}
+    wanted = [x for x in args.legs.split(",") if x]
+    for name in wanted:
+        steps = args.steps
+        warm = args.warmup
+        log("[bench] leg %s: %d warmup + %d timed steps" % (name, warm, steps))
+        r = run_leg(name, steps, warm)
+        if name in ("gauss", "topk"):
+            pages, toks = selection_stats()
+            rows = support_rows(True)
+            kbytes = toks * D * e
+            vbytes = rows * D * e
+            mbytes = meta_gauss_bytes if name == "gauss" else meta_bbox_bytes
+            r.update(selected_pages=pages, selected_tokens=toks, support_v_rows=rows,
+                     bytes={"metadata": mbytes, "tail_refresh": tail_bytes,
+                            "selected_k": kbytes, "support_v": vbytes})
+            step_bytes = mbytes + tail_bytes + kbytes + vbytes
+            sel_positions = pages * P
+            r["kernel_bytes"] = {
+                "score_gauss" if name == "gauss" else "score_bbox":
+                    mbytes + n_pages_total * H * G * (8 if name == "gauss" else 4),
+                "entmax_scores": kbytes + sel_positions * G * 4,
+            }
+        elif name == "entmax_full":
+            rows = support_rows(False)
+            kbytes = tokens_total * H * D * e
+            r.update(support_v_rows=rows,
+                     bytes={"k": kbytes, "support_v": rows * D * e})
+            step_bytes = kbytes + rows * D * e
+            r["kernel_bytes"] = {"entmax_scores": kbytes + n_pages_total * P * H * G * 4}
+        else:
+            step_bytes = 2 * tokens_total * H * D * e
+            r.update(bytes={"kv": step_bytes})
+            r["kernel_bytes"] = {"softmax": step_bytes}
+        r["step_bytes"] = step_bytes
+        r["hbm_gbps"] = step_bytes / (r["median_ms"] * 1e-3) / 1e9
+        r["tokens_per_s"] = B / (r["median_ms"] * 1e-3)
+        results[name] = r
+        log("[bench] %s: median %.1f us, %.0f tokens/s, %.0f GB/s" % (
+            name, r["median_ms"] * 1e3, r["tokens_per_s"], r["hbm_gbps"]))
+
+    head = results.get("gauss") or next(iter(results.values()))
+    head_name = "gauss" if "gauss" in results else next(iter(results))
+    # Dominant kernel of the headline step and its roofline.
+    kb = head["kernel_bytes"]
+    dom = max(kb, key=lambda kname: head["phase_ms"][kname])
+    dom_ms = head["phase_ms"][dom]
+    achieved = kb[dom] / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms}
+
+    speedups = {}
+    for base in ("softmax_full", "entmax_full"):
+        if base in results and head_name in results:
+            speedups["%s_over_%s" % (head_name, base)] = round(
+                results[base]["median_ms"] / head["median_ms"], 3)
+        if base in results and "topk" in results:
+            speedups["topk_over_%s" % base] = round(
+                results[base]["median_ms"] / results["topk"]["median_ms"], 3)
+
+    cpu = None
+    if args.cpu_units > 0:
+        cpu = cpu_baseline(inp, spec, args.cpu_units, alpha, delta, log)
+
+    line = {
+        "metric": "decode tokens/s at 1M ctx (1 GPU); achieved HBM GB/s vs peak",
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["median_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": B, "seq_len": inp.lens[0] if B == 1 else list(inp.lens),
+                   "kv_heads": H, "group": G, "head_dim": D, "page_size": P,
+                   "kv_dtype": spec.kv_dtype, "alpha": alpha, "selector": head_name,
+                   "delta": delta, "topk": k_top, "parallelism": "single GPU",
+                   "cache_flush_between_steps": flush is not None},
+        "hbm_gbps": round(head["hbm_gbps"], 1),
+        "hbm_frac_of_peak": round(head["hbm_gbps"] / PEAK_HBM_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "speedups": speedups,
+        "meta_build_ms": round(meta_build_ms, 4),
+        "legs": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                     for kk, vv in v.items()} for k, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, spec, n_units, alpha, delta, log):
+    """Time the fp64 oracle on a bounded sample of the same step."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover - threadpoolctl is installed here
+        limiter = None
+    P, G, D = spec.page_size, spec.group, spec.head_dim
+    scale = 1.0 / math.sqrt(D)
+    times = []
+    for u in range(n_units):
+        b, h = divmod(u, spec.num_kv_heads)
+        n = inp.lens[b]
+        rows = inp.page_table[b, :(n + P - 1) // P].long()
+        keys = inp.k[rows, h].reshape(-1, D)[:n].double().cpu().numpy()
+        vals = inp.v[rows, h].reshape(-1, D)[:n].double().cpu().numpy()
+        qs = inp.q[b, h * G:(h + 1) * G].double().cpu().numpy()
+        log("[bench] oracle unit %d (%d tokens)" % (u, n))
+        t0 = time.perf_counter()
+        O.decode_unit(qs, keys, vals, P, scale, alpha, "gauss", delta=delta)
+        times.append(time.perf_counter() - t0)
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_unit = statistics.mean(times)
+    units_per_step = spec.batch * spec.num_kv_heads
+    step_s = per_unit * units_per_step
+    return {"value": round(spec.batch / step_s, 6), "unit": "tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) units of one decode step "
+                      "(metadata build, Gaussian scoring, threshold estimate, "
+                      "selection, entmax over the kept pages), fp64 numpy, "
+                      "%.2f s per unit; step time = per-unit time x %d units"
+                      % (n_units, units_per_step, per_unit, units_per_step)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+/*
+ * entmaxkv.h - C ABI of the EntmaxKV support-aware paged decode library
+ * (HIP, AMD CDNA4 / gfx950).
+ *
+ * The method is the one described by the web pages "Technical Summary:
+ * EntmaxKV - Support-Aware Decoding for Entmax Attention" (gist.science) and
+ * the arXiv abstract "EntmaxKV: Support-Aware Decoding for Entmax Attention"
+ * (mlsanity.com index).  One decode step for a query reads lightweight
+ * per-page key summaries, scores every page against the query, selects
+ * candidate pages, gathers only those pages' keys and values through the page
+ * table and runs alpha-entmax attention over them (Technical Summary, §2 A-C).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a DEVICE pointer unless stated otherwise; the
+ *    two structs below are HOST structs, read during the call only.
+ *  - The caller allocates and owns every buffer.  The library never
+ *    allocates or frees device memory, never synchronises and never copies
+ *    device to host.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream).  Results are valid once the caller
+ *    has synchronised with that stream.
+ *  - Unit: one (sequence b, KV head h) pair.  Query heads of KV head h are
+ *    h*G .. h*G+G-1 (grouped-query attention with group size G); one page
+ *    selection is made per unit and shared by its G query heads.
+ *  - Scores: s_i = scale * <q, k_i>.  Entmax argument z_i = (alpha-1) s_i,
+ *    threshold tau, exponent r = 1/(alpha-1): p_i = max(z_i - tau, 0)^r with
+ *    sum_i p_i = 1 (alpha > 1; alpha = 2 is sparsemax).
+ *  - Validation happens on the host before anything is launched; a failed
+ *    validation returns EKV_ERR_INVALID_ARG or EKV_ERR_UNSUPPORTED and
+ *    launches nothing.  A failed launch returns EKV_ERR_HIP.
+ *    ekv_last_error() gives a message for the calling thread's last failure.
+ *  - Device-resident contract (not checked): page_table entries for logical
+ *    pages < ceil(seq_lens[b]/P) are in [0, num_slots); 1 <= seq_lens[b] <=
+ *    max_pages * P; selection lists hold ascending, distinct logical pages
+ *    below ceil(seq_lens[b]/P) with 1 <= count <= that page count.
+ *  - Determinism: identical inputs give bit-identical outputs (no floating
+ *    point atomics; every reduction has a fixed order).
+ *  - Concurrency: no global mutable state besides the per-thread error text;
+ *    calls on different streams with disjoint outputs and workspaces may run
+ *    concurrently.
+ */
+#ifndef ENTMAXKV_H
+#define ENTMAXKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EKV_VERSION 10000 /* 1.0.0 */
+
+typedef enum ekv_status {
+  EKV_OK = 0,
+  EKV_ERR_INVALID_ARG = 1, /* null pointer, bad size, alpha <= 1, ...      */
+  EKV_ERR_UNSUPPORTED = 2, /* valid but not built: D, P, G or dtype        */
+  EKV_ERR_WORKSPACE = 3,   /* workspace missing, short or misaligned       */
+  EKV_ERR_HIP = 4          /* a HIP launch reported an error               */
+} ekv_status;
+
+typedef enum ekv_dtype {
+  EKV_F32 = 0,
+  EKV_BF16 = 1
+} ekv_dtype;
+
+/* Scoring modes (bit flags, may be combined). */
+#define EKV_SCORE_BBOX 1
+#define EKV_SCORE_GAUSS 2
+
+/* Operations for ekv_workspace_size. */
+#define EKV_OP_SELECT_TOPK 1
+#define EKV_OP_SELECT_GAUSS 2
+#define EKV_OP_ENTMAX_DECODE 3
+#define EKV_OP_SOFTMAX_DECODE 4
+
+/*
+ * Paged KV cache (Technical Summary, §2 and §2.A: the cache is cut into
+ * fixed-size pages).  Physical pages ("slots") live in one pool; each
+ * sequence maps its logical pages to slots through its page-table row.
+ *   k, v        [num_slots][num_kv_heads][page_size][head_dim], kv_dtype
+ *   page_table  [batch][max_pages] int32 logical page -> slot
+ *   seq_lens    [batch] int32 valid tokens of each sequence
+ * Supported: head_dim in {64, 128}; page_size in {16, 32, 64};
+ * group in {1, 2, 4, 8}; kv_dtype EKV_F32 or EKV_BF16.  k, v and the
+ * metadata arrays must be 16-byte aligned.
+ */
+typedef struct ekv_paged_kv {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_slots;
+  int32_t max_pages;
+  int32_t kv_dtype; /* ekv_dtype */
+  const void *k;
+  const void *v;
+  const int32_t *page_table;
+  const int32_t *seq_lens;
+} ekv_paged_kv;
+
+/*
+ * Per-page key metadata (Technical Summary, §2.A: coordinate-wise minimum
+ * and maximum keys for the box bound; first and second moments for the
+ * Gaussian statistics).
+ *   bbox   [num_slots][num_kv_heads][2][head_dim] in kv_dtype: [0] = kmin,
+ *          [1] = kmax over the page's valid tokens (exact).  May be NULL.
+ *   gauss  [num_slots][num_kv_heads][2][head_dim] float32: [0] = mean,
+ *          [1] = population variance (divide by the valid token count)
+ *          taken about the mean.  May be NULL.
+ */
+typedef struct ekv_meta {
+  void *bbox;
+  float *gauss;
+} ekv_meta;
+
+/*
+ * ekv_build_meta - (re)build page metadata (Technical Summary, §2.A).
+ * Rebuilds logical pages [first_page[b], ceil(seq_lens[b]/P)) of every
+ * sequence b and every KV head; first_page == NULL rebuilds every page.
+ * After appending tokens, passing first_page[b] = (seq_lens[b]-1)/P (the
+ * page that received the token) refreshes only that page; the result is
+ * bit-identical to a full rebuild.  span_hint is an upper bound on the
+ * number of pages per sequence to rebuild, used only to size the launch
+ * (<= 0: max_pages); the result never depends on it.  Null bbox or gauss
+ * in *meta skips that part.
+ */
+ekv_status ekv_build_meta(const ekv_paged_kv *kv, const int32_t *first_page,
+                          int32_t span_hint, const ekv_meta *meta,
+                          void *stream);
+
+/*
+ * ekv_score_pages - query-aware page scoring (Technical Summary, §2.A).
+ *   q      [batch][H_q][head_dim] float32, H_q = num_kv_heads * group.
+ *   mode   EKV_SCORE_BBOX and/or EKV_SCORE_GAUSS.
+ *   ub     [batch][H_q][max_pages] float32 (BBOX): the box upper bound
+ *          scale * sum_d max(q_d kmin_d, q_d kmax_d) of every page's scores.
+ *   gstat  [batch][H_q][max_pages][2] float32 (GAUSS): mean
+ *          scale * <q, mean> and variance scale^2 * sum_d q_d^2 var_d of a
+ *          page key's score under the page's diagonal Gaussian.
+ * Columns >= ceil(seq_lens[b]/P) are left untouched.
+ */
+ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
+                           const float *q, float scale, int32_t mode,
+                           float *ub, float *gstat, void *stream);
+
+/*
+ * ekv_select_topk - fixed-budget selection (Technical Summary, §2.B.1).
+ * For each unit, ranks pages by the largest bound over its G query heads
+ * and keeps the min(k, n_pages) highest; equal bounds favour the lower page
+ * index.  sel [batch][H_kv][max_pages] int32 receives the kept logical
+ * pages in ascending order, count [batch][H_kv] int32 their number.
+ * Workspace: ekv_workspace_size(EKV_OP_SELECT_TOPK, kv, k) bytes.
+ */
+ekv_status ekv_select_topk(const ekv_paged_kv *kv, const float *ub, int32_t k,
+                           int32_t *sel, int32_t *count, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/*
+ * ekv_select_gauss - Gaussian-aware entmax selection (Technical Summary,
+ * §2.B.2).  Per query head, tau_hat solves
+ *   sum_p n_p E[max(Z_p - tau_hat, 0)^r] = 1,
+ *   Z_p ~ N((alpha-1) mu_p, (alpha-1)^2 sigma_p^2)   (mu, sigma^2 = gstat),
+ * i.e. the entmax normalisation with every token of page p drawn from the
+ * page's score Gaussian.  A page is kept for the unit when, for some query
+ * head h of the group, (alpha-1)(mu_hp + sigma_hp sqrt(2 ln n_p)) >
+ * tau_hat_h - delta (the page's estimated largest score exceeds the
+ * threshold minus the margin).  If no page passes, the single page with the
+ * largest margin max_h[(alpha-1) mhat_hp - tau_hat_h] is kept (lower index on
+ * ties).  Outputs: sel/count as for top-k (ascending, count >= 1) and
+ * tau_hat [batch][H_q] float32.  alpha must be 1.5 or 2 (r in {2, 1});
+ * delta >= 0.  Workspace: ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0).
+ */
+ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
+                            float alpha, float delta, int32_t *sel,
+                            int32_t *count, float *tau_hat, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * ekv_entmax_decode - sparse alpha-entmax attention over the selected pages
+ * (Technical Summary, §2.C), gathered through the page table.  For each
+ * query head: z_i = (alpha-1) scale <q, k_i> over the tokens of the
+ * selected pages; tau solves sum_i max(z_i - tau, 0)^r = 1 (exact to
+ * floating-point rounding for alpha in {1.5, 2}, by bisection otherwise);
+ * out = sum_i p_i v_i / sum_i p_i with p_i = max(z_i - tau, 0)^r.
+ *   sel, count   as produced by the selectors; sel == NULL means every page
+ *                of every sequence (the full-cache entmax baseline), and
+ *                count is then ignored.
+ *   out          [batch][H_q][head_dim] float32.
+ *   tau          [batch][H_q] float32 or NULL.
+ *   probs        [batch][H_q][max_pages*P] float32 or NULL (debug): p of
+ *                every logical token, zero outside the selection, over
+ *                [0, seq_lens[b]).
+ * Workspace: ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0).
+ * Runs ekv_entmax_scores, ekv_entmax_threshold, ekv_entmax_apply in order.
+ */
+ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
+                             float scale, float alpha, const int32_t *sel,
+                             const int32_t *count, float *out, float *tau,
+                             float *probs, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/*
+ * The three steps of ekv_entmax_decode, for callers that time or interleave
+ * them.  They must be called in this order with the same kv, sel, count,
+ * alpha and workspace.
+ *   ekv_entmax_scores     gathers the selected keys and writes z to the
+ *                         workspace with per-chunk maxima.
+ *   ekv_entmax_threshold  solves tau per query head (tau may be NULL: it is
+ *                         then kept in the workspace only).
+ *   ekv_entmax_apply      reads values only for tokens with p_i > 0 and
+ *                         writes out (and probs if not NULL).
+ */
+ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
+                             float scale, float alpha, const int32_t *sel,
+                             const int32_t *count, void *ws, size_t ws_bytes,
+                             void *stream);
+ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
+                                const int32_t *sel, const int32_t *count,
+                                float *tau, void *ws, size_t ws_bytes,
+                                void *stream);
+ekv_status ekv_entmax_apply(const ekv_paged_kv *kv, float alpha,
+                            const int32_t *sel, const int32_t *count,
+                            float *out, float *probs, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * ekv_softmax_decode - split-K softmax attention (the full-cache baseline
+ * the Technical Summary, §4, compares against).  Each chunk of pages yields
+ * (running max, sum of exponentials, weighted value sum); a second kernel
+ * merges the chunks in log-sum-exp form.  sel/count as above (NULL sel =
+ * full cache).  out [batch][H_q][head_dim] float32; lse [batch][H_q]
+ * float32 (natural log of sum_i exp(s_i)) or NULL.
+ * Workspace: ekv_workspace_size(EKV_OP_SOFTMAX_DECODE, kv, 0).
+ */
+ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
+                              float scale, const int32_t *sel,
+                              const int32_t *count, float *out, float *lse,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of workspace an operation needs (host only; 0 on invalid input). */
+size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0);
+
+/* Static description of a status code (host only). */
+const char *ekv_status_string(ekv_status s);
+
+/* Message describing the calling thread's most recent failure (host only). */
+const char *ekv_last_error(void);
+
+/* EKV_VERSION of the built library (host only). */
+int32_t ekv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAXKV_H */

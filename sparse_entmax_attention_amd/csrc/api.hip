@@ -1,0 +1,341 @@
+// C ABI of the EntmaxKV paged decode library: host-side validation,
+// workspace sizing and dispatch to the kernel instances.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <type_traits>
+
+#include "ekv_device.h"
+#include "ekv_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ekv_status fail(ekv_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+ekv_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return EKV_OK;
+  return fail(EKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Checks of the paged cache common to every entry point.
+ekv_status check_kv(const ekv_paged_kv *kv, bool need_k, bool need_v) {
+  if (!kv) return fail(EKV_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->group < 1 ||
+      kv->head_dim < 1 || kv->page_size < 1 || kv->num_slots < 1 ||
+      kv->max_pages < 1)
+    return fail(EKV_ERR_INVALID_ARG,
+                "sizes must be >= 1 (batch %d, heads %d, group %d, D %d, P %d, "
+                "slots %d, max_pages %d)",
+                kv->batch, kv->num_kv_heads, kv->group, kv->head_dim,
+                kv->page_size, kv->num_slots, kv->max_pages);
+  if (kv->kv_dtype != EKV_F32 && kv->kv_dtype != EKV_BF16)
+    return fail(EKV_ERR_INVALID_ARG, "kv_dtype %d is not an ekv_dtype",
+                kv->kv_dtype);
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(EKV_ERR_UNSUPPORTED, "head_dim %d (built: 64, 128)",
+                kv->head_dim);
+  if (kv->page_size != 16 && kv->page_size != 32 && kv->page_size != 64)
+    return fail(EKV_ERR_UNSUPPORTED, "page_size %d (built: 16, 32, 64)",
+                kv->page_size);
+  if (kv->group != 1 && kv->group != 2 && kv->group != 4 && kv->group != 8)
+    return fail(EKV_ERR_UNSUPPORTED, "group %d (built: 1, 2, 4, 8)",
+                kv->group);
+  const double cells = static_cast<double>(kv->max_pages) * kv->page_size;
+  if (cells > 2147483647.0)
+    return fail(EKV_ERR_UNSUPPORTED, "max_pages * page_size exceeds 2^31-1");
+  if (!kv->page_table || !kv->seq_lens)
+    return fail(EKV_ERR_INVALID_ARG, "page_table and seq_lens are required");
+  if (need_k && (!kv->k || !aligned(kv->k, 16)))
+    return fail(EKV_ERR_INVALID_ARG, "k must be non-NULL and 16-byte aligned");
+  if (need_v && (!kv->v || !aligned(kv->v, 16)))
+    return fail(EKV_ERR_INVALID_ARG, "v must be non-NULL and 16-byte aligned");
+  return EKV_OK;
+}
+
+ekv_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return EKV_OK;
+  if (!ws) return fail(EKV_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (ws_bytes < need)
+    return fail(EKV_ERR_WORKSPACE, "workspace has %zu bytes, %zu required",
+                ws_bytes, need);
+  if (!aligned(ws, 256))
+    return fail(EKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return EKV_OK;
+}
+
+ekv_status check_alpha(float alpha) {
+  if (!std::isfinite(alpha) || !(alpha > 1.0f))
+    return fail(EKV_ERR_INVALID_ARG, "alpha must be finite and > 1 (got %g)",
+                static_cast<double>(alpha));
+  return EKV_OK;
+}
+
+ekv_status check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(EKV_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)",
+                static_cast<double>(scale));
+  return EKV_OK;
+}
+
+ekv_status check_sel(const int32_t *sel, const int32_t *count) {
+  if (sel && !count)
+    return fail(EKV_ERR_INVALID_ARG, "count is required with sel");
+  return EKV_OK;
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Calls f(E{}, IC<D>{}, IC<G>{}) for the runtime (dtype, D, G).
+template <class F>
+hipError_t with_edg(const ekv_paged_kv &kv, F &&f) {
+  auto on_g = [&](auto e, auto d) -> hipError_t {
+    switch (kv.group) {
+      case 1: return f(e, d, IC<1>{});
+      case 2: return f(e, d, IC<2>{});
+      case 4: return f(e, d, IC<4>{});
+      default: return f(e, d, IC<8>{});
+    }
+  };
+  auto on_d = [&](auto e) -> hipError_t {
+    if (kv.head_dim == 64) return on_g(e, IC<64>{});
+    return on_g(e, IC<128>{});
+  };
+  if (kv.kv_dtype == EKV_F32) return on_d(ekv::F32{});
+  return on_d(ekv::BF16{});
+}
+
+template <class F>
+hipError_t with_g(const ekv_paged_kv &kv, F &&f) {
+  switch (kv.group) {
+    case 1: return f(IC<1>{});
+    case 2: return f(IC<2>{});
+    case 4: return f(IC<4>{});
+    default: return f(IC<8>{});
+  }
+}
+
+#define EKV_TRY(x)                        \
+  do {                                    \
+    const ekv_status s_ = (x);            \
+    if (s_ != EKV_OK) return s_;          \
+  } while (0)
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
+  (void)k_or_0;
+  if (check_kv(kv, false, false) != EKV_OK) return 0;
+  const size_t units = static_cast<size_t>(kv->batch) * kv->num_kv_heads;
+  switch (op) {
+    case EKV_OP_SELECT_TOPK:
+      return ((units * kv->max_pages * 4) + 255) & ~static_cast<size_t>(255);
+    case EKV_OP_SELECT_GAUSS:
+      return 0;
+    case EKV_OP_ENTMAX_DECODE:
+      return ekv::decode_ws_layout(*kv).total;
+    case EKV_OP_SOFTMAX_DECODE:
+      return ekv::softmax_ws_layout(*kv).total;
+    default:
+      return 0;
+  }
+}
+
+ekv_status ekv_build_meta(const ekv_paged_kv *kv, const int32_t *first_page,
+                          int32_t span_hint, const ekv_meta *meta,
+                          void *stream) {
+  EKV_TRY(check_kv(kv, true, false));
+  if (!meta) return fail(EKV_ERR_INVALID_ARG, "meta is NULL");
+  if (!meta->bbox && !meta->gauss)
+    return fail(EKV_ERR_INVALID_ARG, "meta has neither bbox nor gauss");
+  if ((meta->bbox && !aligned(meta->bbox, 16)) ||
+      (meta->gauss && !aligned(meta->gauss, 16)))
+    return fail(EKV_ERR_INVALID_ARG, "metadata must be 16-byte aligned");
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto) {
+    return ekv::launch_build_meta<decltype(E), decltype(D)::value>(
+        *kv, first_page, span_hint, *meta, as_stream(stream));
+  });
+  return hip_status(e, "ekv_build_meta launch");
+}
+
+ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
+                           const float *q, float scale, int32_t mode,
+                           float *ub, float *gstat, void *stream) {
+  EKV_TRY(check_kv(kv, false, false));
+  EKV_TRY(check_scale(scale));
+  if (!meta || !q) return fail(EKV_ERR_INVALID_ARG, "meta and q are required");
+  if (mode <= 0 || (mode & ~(EKV_SCORE_BBOX | EKV_SCORE_GAUSS)))
+    return fail(EKV_ERR_INVALID_ARG, "mode %d is not a set of EKV_SCORE_*", mode);
+  if ((mode & EKV_SCORE_BBOX) && (!meta->bbox || !ub))
+    return fail(EKV_ERR_INVALID_ARG, "box scoring needs meta->bbox and ub");
+  if ((mode & EKV_SCORE_GAUSS) && (!meta->gauss || !gstat))
+    return fail(EKV_ERR_INVALID_ARG, "Gaussian scoring needs meta->gauss and gstat");
+  if ((meta->bbox && !aligned(meta->bbox, 16)) ||
+      (meta->gauss && !aligned(meta->gauss, 16)) || !aligned(q, 16) ||
+      (gstat && !aligned(gstat, 8)))
+    return fail(EKV_ERR_INVALID_ARG, "q/metadata must be 16-byte aligned, gstat 8");
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
+    return ekv::launch_score<decltype(E), decltype(D)::value,
+                             decltype(G)::value>(*kv, *meta, q, scale, mode,
+                                                 ub, gstat, as_stream(stream));
+  });
+  return hip_status(e, "ekv_score_pages launch");
+}
+
+ekv_status ekv_select_topk(const ekv_paged_kv *kv, const float *ub, int32_t k,
+                           int32_t *sel, int32_t *count, void *ws,
+                           size_t ws_bytes, void *stream) {
+  EKV_TRY(check_kv(kv, false, false));
+  if (!ub || !sel || !count)
+    return fail(EKV_ERR_INVALID_ARG, "ub, sel and count are required");
+  if (k < 1) return fail(EKV_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_SELECT_TOPK, kv, k)));
+  const hipError_t e = with_g(*kv, [&](auto G) {
+    return ekv::launch_select_topk<decltype(G)::value>(*kv, ub, k, sel, count,
+                                                      ws, as_stream(stream));
+  });
+  return hip_status(e, "ekv_select_topk launch");
+}
+
+ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
+                            float alpha, float delta, int32_t *sel,
+                            int32_t *count, float *tau_hat, void *ws,
+                            size_t ws_bytes, void *stream) {
+  EKV_TRY(check_kv(kv, false, false));
+  EKV_TRY(check_alpha(alpha));
+  if (alpha != 1.5f && alpha != 2.0f)
+    return fail(EKV_ERR_UNSUPPORTED,
+                "Gaussian selector built for alpha in {1.5, 2} (got %g)",
+                static_cast<double>(alpha));
+  if (std::isnan(delta) || delta < 0.0f)
+    return fail(EKV_ERR_INVALID_ARG, "delta must be >= 0 (got %g)",
+                static_cast<double>(delta));
+  if (!gstat || !sel || !count || !tau_hat)
+    return fail(EKV_ERR_INVALID_ARG, "gstat, sel, count and tau_hat are required");
+  if (!aligned(gstat, 8)) return fail(EKV_ERR_INVALID_ARG, "gstat must be 8-byte aligned");
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0)));
+  const hipError_t e = with_g(*kv, [&](auto G) {
+    return ekv::launch_select_gauss<decltype(G)::value>(
+        *kv, gstat, alpha, delta, sel, count, tau_hat, as_stream(stream));
+  });
+  return hip_status(e, "ekv_select_gauss launch");
+}
+
+ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
+                             float scale, float alpha, const int32_t *sel,
+                             const int32_t *count, void *ws, size_t ws_bytes,
+                             void *stream) {
+  EKV_TRY(check_kv(kv, true, false));
+  EKV_TRY(check_scale(scale));
+  EKV_TRY(check_alpha(alpha));
+  EKV_TRY(check_sel(sel, count));
+  if (!q || !aligned(q, 16))
+    return fail(EKV_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0)));
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
+    return ekv::launch_entmax_scores<decltype(E), decltype(D)::value,
+                                     decltype(G)::value>(
+        *kv, q, scale, alpha, sel, count, ws, as_stream(stream));
+  });
+  return hip_status(e, "ekv_entmax_scores launch");
+}
+
+ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
+                                const int32_t *sel, const int32_t *count,
+                                float *tau, void *ws, size_t ws_bytes,
+                                void *stream) {
+  EKV_TRY(check_kv(kv, false, false));
+  EKV_TRY(check_alpha(alpha));
+  EKV_TRY(check_sel(sel, count));
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0)));
+  const hipError_t e = with_g(*kv, [&](auto G) {
+    return ekv::launch_entmax_threshold<decltype(G)::value>(
+        *kv, alpha, sel, count, tau, ws, as_stream(stream));
+  });
+  return hip_status(e, "ekv_entmax_threshold launch");
+}
+
+ekv_status ekv_entmax_apply(const ekv_paged_kv *kv, float alpha,
+                            const int32_t *sel, const int32_t *count,
+                            float *out, float *probs, void *ws,
+                            size_t ws_bytes, void *stream) {
+  EKV_TRY(check_kv(kv, false, true));
+  EKV_TRY(check_alpha(alpha));
+  EKV_TRY(check_sel(sel, count));
+  if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0)));
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
+    return ekv::launch_entmax_apply<decltype(E), decltype(D)::value,
+                                    decltype(G)::value>(
+        *kv, alpha, sel, count, out, probs, ws, as_stream(stream));
+  });
+  return hip_status(e, "ekv_entmax_apply launch");
+}
+
+ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
+                             float scale, float alpha, const int32_t *sel,
+                             const int32_t *count, float *out, float *tau,
+                             float *probs, void *ws, size_t ws_bytes,
+                             void *stream) {
+  EKV_TRY(check_kv(kv, true, true));
+  if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
+  EKV_TRY(ekv_entmax_scores(kv, q, scale, alpha, sel, count, ws, ws_bytes, stream));
+  EKV_TRY(ekv_entmax_threshold(kv, alpha, sel, count, tau, ws, ws_bytes, stream));
+  return ekv_entmax_apply(kv, alpha, sel, count, out, probs, ws, ws_bytes, stream);
+}
+
+ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
+                              float scale, const int32_t *sel,
+                              const int32_t *count, float *out, float *lse,
+                              void *ws, size_t ws_bytes, void *stream) {
+  EKV_TRY(check_kv(kv, true, true));
+  EKV_TRY(check_scale(scale));
+  EKV_TRY(check_sel(sel, count));
+  if (!q || !aligned(q, 16) || !out)
+    return fail(EKV_ERR_INVALID_ARG, "q (16-byte aligned) and out are required");
+  EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_SOFTMAX_DECODE, kv, 0)));
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
+    return ekv::launch_softmax<decltype(E), decltype(D)::value,
+                               decltype(G)::value>(*kv, q, scale, sel, count,
+                                                   out, lse, ws,
+                                                   as_stream(stream));
+  });
+  return hip_status(e, "ekv_softmax_decode launch");
+}
+
+const char *ekv_status_string(ekv_status s) {
+  switch (s) {
+    case EKV_OK: return "EKV_OK";
+    case EKV_ERR_INVALID_ARG: return "EKV_ERR_INVALID_ARG";
+    case EKV_ERR_UNSUPPORTED: return "EKV_ERR_UNSUPPORTED";
+    case EKV_ERR_WORKSPACE: return "EKV_ERR_WORKSPACE";
+    case EKV_ERR_HIP: return "EKV_ERR_HIP";
+  }
+  return "EKV_UNKNOWN_STATUS";
+}
+
+const char *ekv_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ekv_version(void) { return EKV_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Device-side helpers shared by the EntmaxKV HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "entmaxkv.h"
+
+namespace ekv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element access.  K/V and box metadata are float32 or bfloat16; a bfloat16
+// is the high half of a float32, so widening is a shift (exact).
+// ---------------------------------------------------------------------------
+struct F32 {
+  using T = float;
+  static constexpr int kBytes = 4;
+};
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Load 8 consecutive elements starting at p (16-byte aligned for bf16,
+// 32-byte for f32) and widen them to float.
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4 *>(p);
+  x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x);
+  x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
+  x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z);
+  x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
+}
+
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t *p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+__device__ __forceinline__ void store1(float *p, float x) { *p = x; }
+// Only used for values that are already exactly representable in bfloat16
+// (minima and maxima of bfloat16 keys), so truncation is exact.
+__device__ __forceinline__ void store1(uint16_t *p, float x) {
+  *p = static_cast<uint16_t>(__float_as_uint(x) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Lane-group reductions.  W lanes (power of two, <= 64) that are contiguous
+// and W-aligned reduce to a value present in every lane of the group.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+template <int W>
+__device__ __forceinline__ double group_sum_d(double x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+template <int W>
+__device__ __forceinline__ int group_sum_i(int x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a block of NT threads; also returns the total.
+// `smem` must hold NT/64 ints.  Contains barriers: call from all threads.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, int *smem, int &total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(x);
+  __syncthreads();
+  if (lane == kWave - 1) smem[wid] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int v = smem[w];
+    base += (w < wid) ? v : 0;
+    tot += v;
+  }
+  total = tot;
+  return base + incl - x;
+}
+
+// Block-wide reductions of NT threads; result valid in every thread.
+// `smem` must hold NT/64 elements.  Contain barriers.
+template <int NT>
+__device__ __forceinline__ float block_max(float x, float *smem) {
+  constexpr int NW = NT / kWave;
+  x = group_max<kWave>(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
+  __syncthreads();
+  float r = smem[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmaxf(r, smem[w]);
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ double block_sum_d(double x, double *smem) {
+  constexpr int NW = NT / kWave;
+  x = group_sum_d<kWave>(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
+  __syncthreads();
+  double r = smem[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += smem[w];
+  return r;
+}
+template <int NT>
+__device__ __forceinline__ int block_sum_i(int x, int *smem) {
+  constexpr int NW = NT / kWave;
+  x = group_sum_i<kWave>(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = smem[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += smem[w];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Paged layout helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int n_pages_of(int len, int P) {
+  return (len + P - 1) / P;
+}
+// Valid tokens of logical page lp of a sequence of length len.
+__device__ __forceinline__ int page_tokens(int lp, int len, int P) {
+  const int r = len - lp * P;
+  return r < P ? r : P;
+}
+// Element offset of row (slot, head, token) in a [slots][H][P][D] pool.
+__device__ __forceinline__ size_t pool_row(int slot, int h, int t, int H,
+                                           int P, int D) {
+  return ((static_cast<size_t>(slot) * H + h) * P + t) * static_cast<size_t>(D);
+}
+// Element offset of metadata row (slot, head, which) in [slots][H][2][D].
+__device__ __forceinline__ size_t meta_row(int slot, int h, int which, int H,
+                                           int D) {
+  return ((static_cast<size_t>(slot) * H + h) * 2 + which) *
+         static_cast<size_t>(D);
+}
+
+}  // namespace ekv

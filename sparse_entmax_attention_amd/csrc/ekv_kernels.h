@@ -1,0 +1,77 @@
+// Host-side launchers of the EntmaxKV kernels, one template instance per
+// (element type, head_dim, group) combination the library is built for.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "entmaxkv.h"
+
+namespace ekv {
+
+struct F32;
+struct BF16;
+
+// Tokens covered by one decode work item (a "chunk" of selected pages).
+constexpr int kChunkTokens = 512;
+
+inline int chunk_pages(int P) { return kChunkTokens / P; }
+inline int max_chunks(const ekv_paged_kv &kv) {
+  const int ppc = chunk_pages(kv.page_size);
+  return (kv.max_pages + ppc - 1) / ppc;
+}
+
+// Decode workspace layout (offsets in bytes, each 256-byte aligned).
+struct DecodeWs {
+  size_t z, cmax, tau, part_o, part_s, total;
+};
+DecodeWs decode_ws_layout(const ekv_paged_kv &kv);
+struct SoftmaxWs {
+  size_t part_m, part_l, part_o, total;
+};
+SoftmaxWs softmax_ws_layout(const ekv_paged_kv &kv);
+
+template <class E, int D>
+hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
+                             int span, const ekv_meta &meta,
+                             hipStream_t stream);
+template <class E, int D, int G>
+hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
+                        const float *q, float scale, int mode, float *ub,
+                        float *gstat, hipStream_t stream);
+template <int G>
+hipError_t launch_select_topk(const ekv_paged_kv &kv, const float *ub, int k,
+                              int32_t *sel, int32_t *count, void *ws,
+                              hipStream_t stream);
+template <int G>
+hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
+                               float alpha, float delta, int32_t *sel,
+                               int32_t *count, float *tau_hat,
+                               hipStream_t stream);
+template <class E, int D, int G>
+hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
+                                float scale, float alpha, const int32_t *sel,
+                                const int32_t *count, void *ws,
+                                hipStream_t stream);
+template <int G>
+hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
+                                   const int32_t *sel, const int32_t *count,
+                                   float *tau, void *ws, hipStream_t stream);
+template <class E, int D, int G>
+hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
+                               const int32_t *sel, const int32_t *count,
+                               float *out, float *probs, void *ws,
+                               hipStream_t stream);
+template <class E, int D, int G>
+hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
+                          const int32_t *sel, const int32_t *count, float *out,
+                          float *lse, void *ws, hipStream_t stream);
+
+#define EKV_FOR_EACH_G(X) X(1) X(2) X(4) X(8)
+#define EKV_FOR_EACH_ED(X) X(F32, 64) X(F32, 128) X(BF16, 64) X(BF16, 128)
+#define EKV_FOR_EACH_EDG(X)                                                \
+  X(F32, 64, 1) X(F32, 64, 2) X(F32, 64, 4) X(F32, 64, 8)                  \
+  X(F32, 128, 1) X(F32, 128, 2) X(F32, 128, 4) X(F32, 128, 8)              \
+  X(BF16, 64, 1) X(BF16, 64, 2) X(BF16, 64, 4) X(BF16, 64, 8)              \
+  X(BF16, 128, 1) X(BF16, 128, 2) X(BF16, 128, 4) X(BF16, 128, 8)
+
+}  // namespace ekv

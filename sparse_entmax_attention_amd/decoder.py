@@ -1,0 +1,92 @@
+"""Device buffers for the EntmaxKV decode step, and the step itself.
+
+:class:`DecodeBuffers` allocates (once) every output and workspace the entry
+points need for one paged cache and calls them in pipeline order.  It holds
+no arithmetic: each method is a sequence of C-ABI calls.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+class DecodeBuffers:
+    """Outputs and workspaces of one paged cache's decode step.
+
+    kv: a :class:`PagedKV`.  bbox / gauss select which metadata to keep.
+    """
+
+    def __init__(self, kv: B.PagedKV, bbox: bool = True, gauss: bool = True,
+                 softmax: bool = False):
+        self.kv = kv
+        dev = kv.device
+        S, H, D = kv.num_slots, kv.num_kv_heads, kv.head_dim
+        Bt, Hq, MP = kv.batch, kv.num_q_heads, kv.max_pages
+        self.scale = 1.0 / math.sqrt(D)
+        self.bbox = torch.empty(S, H, 2, D, dtype=kv.k.dtype, device=dev) if bbox else None
+        self.gauss = torch.empty(S, H, 2, D, dtype=torch.float32, device=dev) if gauss else None
+        self.ub = torch.empty(Bt, Hq, MP, dtype=torch.float32, device=dev) if bbox else None
+        self.gstat = torch.empty(Bt, Hq, MP, 2, dtype=torch.float32, device=dev) if gauss else None
+        self.sel = torch.empty(Bt, H, MP, dtype=torch.int32, device=dev)
+        self.count = torch.empty(Bt, H, dtype=torch.int32, device=dev)
+        self.tau_hat = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
+        self.tau = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(Bt, Hq, D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
+        self.ws_topk = self._ws(B.EKV_OP_SELECT_TOPK)
+        self.ws_gauss = self._ws(B.EKV_OP_SELECT_GAUSS)
+        self.ws_decode = self._ws(B.EKV_OP_ENTMAX_DECODE)
+        self.ws_softmax = self._ws(B.EKV_OP_SOFTMAX_DECODE) if softmax else None
+
+    def _ws(self, op: int) -> Optional[torch.Tensor]:
+        n = B.ekv_workspace_size(op, self.kv, 1)
+        if n == 0:
+            return None
+        return torch.empty(n, dtype=torch.uint8, device=self.kv.device)
+
+    # -- pipeline steps ------------------------------------------------------
+    def build_meta(self, first_page=None, span_hint: int = 0, stream=None):
+        B.ekv_build_meta(self.kv, self.bbox, self.gauss, first_page, span_hint,
+                         stream)
+
+    def score(self, q, mode: int, stream=None):
+        B.ekv_score_pages(self.kv, self.bbox, self.gauss, q, self.scale, mode,
+                          self.ub if mode & B.EKV_SCORE_BBOX else None,
+                          self.gstat if mode & B.EKV_SCORE_GAUSS else None,
+                          stream)
+
+    def select_topk(self, k: int, stream=None):
+        B.ekv_select_topk(self.kv, self.ub, k, self.sel, self.count,
+                          self.ws_topk, stream)
+
+    def select_gauss(self, alpha: float, delta: float, stream=None):
+        B.ekv_select_gauss(self.kv, self.gstat, alpha, delta, self.sel,
+                           self.count, self.tau_hat, self.ws_gauss, stream)
+
+    def entmax(self, q, alpha: float, selected: bool = True, probs=None,
+               stream=None):
+        B.ekv_entmax_decode(self.kv, q, self.scale, alpha,
+                            self.sel if selected else None,
+                            self.count if selected else None, self.out,
+                            self.tau, probs, self.ws_decode, stream)
+
+    def softmax(self, q, selected: bool = False, stream=None):
+        B.ekv_softmax_decode(self.kv, q, self.scale,
+                             self.sel if selected else None,
+                             self.count if selected else None, self.out,
+                             self.lse, self.ws_softmax, stream)
+
+    # -- whole steps ---------------------------------------------------------
+    def step_topk(self, q, alpha: float, k: int, stream=None):
+        self.score(q, B.EKV_SCORE_BBOX, stream)
+        self.select_topk(k, stream)
+        self.entmax(q, alpha, True, None, stream)
+
+    def step_gauss(self, q, alpha: float, delta: float, stream=None):
+        self.score(q, B.EKV_SCORE_GAUSS, stream)
+        self.select_gauss(alpha, delta, stream)
+        self.entmax(q, alpha, True, None, stream)

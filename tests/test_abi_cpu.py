@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load, export every function the header declares, and
+reject invalid arguments on the host before anything is launched.  The
+pointers handed in below are never dereferenced by the host code (only
+checked for NULL and alignment), and every call here fails validation, so
+no device work is ever started.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_entmax_attention_amd import _binding as B
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "entmaxkv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ekv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B._SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert B.ekv_version() == 10000
+    for code, name in [(0, "EKV_OK"), (1, "EKV_ERR_INVALID_ARG"),
+                       (2, "EKV_ERR_UNSUPPORTED"), (3, "EKV_ERR_WORKSPACE"),
+                       (4, "EKV_ERR_HIP")]:
+        assert lib.ekv_status_string(code).decode() == name
+
+
+FAKE = 0x100000  # 1 MiB: 256-byte aligned, never dereferenced on the host
+
+
+def _kv(**kw):
+    d = dict(batch=1, num_kv_heads=8, group=4, head_dim=128, page_size=32,
+             num_slots=1024, max_pages=1024, kv_dtype=B.EKV_BF16, k=FAKE,
+             v=FAKE, page_table=FAKE, seq_lens=FAKE)
+    d.update(kw)
+    return B.ekv_paged_kv(**d)
+
+
+def test_workspace_sizes(lib):
+    kv = _kv()
+    units, G, D, cap = 8, 4, 128, 1024 * 32
+    mc = (1024 + 15) // 16
+    dec = lib.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE, ctypes.byref(kv), 0)
+    assert dec >= units * G * cap * 4 + units * mc * G * D * 4
+    assert dec % 256 == 0
+    topk = lib.ekv_workspace_size(B.EKV_OP_SELECT_TOPK, ctypes.byref(kv), 16)
+    assert topk >= units * 1024 * 4
+    assert lib.ekv_workspace_size(99, ctypes.byref(kv), 0) == 0
+    bad = _kv(head_dim=96)
+    assert lib.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE, ctypes.byref(bad), 0) == 0
+
+
+def _topk(lib, kv, k=16, ub=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.ekv_select_topk(ctypes.byref(kv), ub, k, FAKE, FAKE, ws,
+                               ws_bytes, None)
+
+
+def test_validation_errors(lib):
+    assert _topk(lib, _kv(), k=0) == B.EKV_ERR_INVALID_ARG
+    assert _topk(lib, _kv(), ub=None) == B.EKV_ERR_INVALID_ARG
+    assert _topk(lib, _kv(batch=0)) == B.EKV_ERR_INVALID_ARG
+    assert _topk(lib, _kv(head_dim=96)) == B.EKV_ERR_UNSUPPORTED
+    assert _topk(lib, _kv(page_size=8)) == B.EKV_ERR_UNSUPPORTED
+    assert _topk(lib, _kv(group=3)) == B.EKV_ERR_UNSUPPORTED
+    assert _topk(lib, _kv(kv_dtype=7)) == B.EKV_ERR_INVALID_ARG
+    assert _topk(lib, _kv(page_table=None)) == B.EKV_ERR_INVALID_ARG
+    assert _topk(lib, _kv(), ws=None) == B.EKV_ERR_WORKSPACE
+    assert _topk(lib, _kv(), ws_bytes=16) == B.EKV_ERR_WORKSPACE
+    assert _topk(lib, _kv(), ws=FAKE + 64) == B.EKV_ERR_WORKSPACE
+    assert "k must be >= 1" in (_topk(lib, _kv(), k=0) and
+                                lib.ekv_last_error().decode())
+    kv = _kv()
+    # alpha must exceed 1; the Gaussian selector is built for 1.5 and 2
+    for alpha, want in [(1.0, B.EKV_ERR_INVALID_ARG), (0.5, B.EKV_ERR_INVALID_ARG),
+                        (float("nan"), B.EKV_ERR_INVALID_ARG),
+                        (1.25, B.EKV_ERR_UNSUPPORTED)]:
+        assert lib.ekv_select_gauss(ctypes.byref(kv), FAKE, alpha, 0.5, FAKE,
+                                    FAKE, FAKE, None, 0, None) == want
+    assert lib.ekv_select_gauss(ctypes.byref(kv), FAKE, 1.5, -1.0, FAKE, FAKE,
+                                FAKE, None, 0, None) == B.EKV_ERR_INVALID_ARG
+    # decode: misaligned K, sel without count, non-positive scale, no output
+    ws = 1 << 34
+    assert lib.ekv_entmax_decode(ctypes.byref(_kv(k=FAKE + 2)), FAKE, 0.1, 1.5,
+                                 None, None, FAKE, None, None, FAKE, ws,
+                                 None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.1, 1.5, FAKE, None,
+                                 FAKE, None, None, FAKE, ws,
+                                 None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.0, 1.5, None, None,
+                                 FAKE, None, None, FAKE, ws,
+                                 None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.1, 1.5, None, None,
+                                 None, None, None, FAKE, ws,
+                                 None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_softmax_decode(ctypes.byref(kv), FAKE, 0.1, None, None,
+                                  FAKE, None, FAKE, 16,
+                                  None) == B.EKV_ERR_WORKSPACE
+    m = B.ekv_meta(None, None)
+    assert lib.ekv_build_meta(ctypes.byref(kv), None, 0, ctypes.byref(m),
+                              None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_score_pages(ctypes.byref(kv), ctypes.byref(B.ekv_meta(FAKE, None)),
+                               FAKE, 0.1, B.EKV_SCORE_GAUSS, FAKE, None,
+                               None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_score_pages(ctypes.byref(kv), ctypes.byref(B.ekv_meta(FAKE, FAKE)),
+                               FAKE, 0.1, 4, FAKE, FAKE,
+                               None) == B.EKV_ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    import importlib
+    saved = B._lib_handle
+    try:
+        B._lib_handle = None
+        with pytest.raises(RuntimeError, match="not built"):
+            B.load_library(str(tmp_path / "missing.so"))
+    finally:
+        B._lib_handle = saved

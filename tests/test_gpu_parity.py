@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs are seeded synthetic workloads at sizes the oracle finishes in
+seconds, spanning several chunks and ending in ragged last pages.  The oracle
+gets fp64 copies of the exact bytes on the device.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_entmax_attention_amd as ekv
+import workloads
+from parity_utils import (CUT_REL, OUT_RTOL_L2, TAU_ATOL, HostCopy,
+                          check_gauss_selection, check_topk_selection, f64,
+                          paged_kv, rel_l2, scale_of)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (workload, overrides, seed)
+    "needle4k_f32_d64": ("needle_4k_d64_f32", {}, 100),
+    "needle32k_gqa": ("needle_32k_gqa", {"seq_len": 32768 - 19}, 101),
+    "cluster_b2_ragged": ("cluster_128k_b4", {"batch": 2, "seq_len": 9000}, 102),
+    "cluster_p64": ("cluster_1m", {"seq_len": 65536 + 3}, 103),
+    "pool_permuted": ("ragged_pool_b16", {"batch": 3, "len_range": (700, 6000)}, 104),
+}
+
+_cache = {}
+
+
+def inputs(name, device):
+    if name not in _cache:
+        wl, ov, seed = CASES[name]
+        spec = workloads.workload(wl, **ov)
+        print("[case] %s seed=%d spec=%s" % (name, seed, ov), flush=True)
+        inp = workloads.generate(spec, seed, device)
+        _cache[name] = (inp, HostCopy(inp))
+    return _cache[name]
+
+
+def _units(inp):
+    return [(b, h) for b in range(inp.spec.batch)
+            for h in range(inp.spec.num_kv_heads)]
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_metadata(gpu, name):
+    inp, host = inputs(name, gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    torch.cuda.synchronize()
+    bbox, gauss = f64(buf.bbox), f64(buf.gauss)
+    P = inp.spec.page_size
+    for b, h in _units(inp):
+        _, keys, _ = host.unit(b, h)
+        kmin, kmax, mean, var = O.unit_metadata(keys, P)
+        slots = host.pt[b, :kmin.shape[0]]
+        assert np.array_equal(bbox[slots, h, 0], kmin)
+        assert np.array_equal(bbox[slots, h, 1], kmax)
+        mag = np.maximum(np.abs(kmin), np.abs(kmax))
+        assert (np.abs(gauss[slots, h, 0] - mean) <= 2e-6 * (1 + mag)).all()
+        assert (np.abs(gauss[slots, h, 1] - var) <= 2e-5 * var + 2e-6 * (1 + mag) ** 2).all()
+
+
+def test_incremental_metadata_equals_full_rebuild(gpu):
+    spec = workloads.workload("ragged_pool_b16", batch=4, len_range=(60, 2000))
+    print("[case] incremental metadata, seed 105", flush=True)
+    inp = workloads.generate(spec, 105, gpu)
+    kv = paged_kv(inp)
+    inc = ekv.DecodeBuffers(kv)
+    inc.build_meta()
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(5)
+    for step in range(40):
+        first = workloads.append_token(inp, gen)
+        inc.build_meta(first, span_hint=1)
+    full = ekv.DecodeBuffers(paged_kv(inp))
+    full.build_meta()
+    torch.cuda.synchronize()
+    P = spec.page_size
+    for b in range(spec.batch):
+        slots = inp.page_table[b, :(inp.lens[b] + P - 1) // P].long()
+        assert torch.equal(inc.bbox[slots], full.bbox[slots])
+        assert torch.equal(inc.gauss[slots], full.gauss[slots])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_page_scores(gpu, name):
+    inp, host = inputs(name, gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.score(inp.q, ekv.EKV_SCORE_BBOX | ekv.EKV_SCORE_GAUSS)
+    torch.cuda.synchronize()
+    ub, gstat = f64(buf.ub), f64(buf.gstat)
+    P, G, sc = inp.spec.page_size, inp.spec.group, scale_of(inp.spec)
+    for b, h in _units(inp):
+        qs, keys, _ = host.unit(b, h)
+        kmin, kmax, mean, var = O.unit_metadata(keys, P)
+        n = kmin.shape[0]
+        for g in range(G):
+            q = qs[g]
+            ref = O.bbox_bound(q, kmin, kmax, sc)
+            mag = sc * (np.abs(q)[None] * np.maximum(np.abs(kmin), np.abs(kmax))).sum(1)
+            got = ub[b, h * G + g, :n]
+            assert (np.abs(got - ref) <= 3e-5 * mag + 1e-6).all()
+            mu, s2 = O.gauss_moments(q, mean, var, sc)
+            magm = sc * (np.abs(q)[None] * np.abs(mean)).sum(1)
+            assert (np.abs(gstat[b, h * G + g, :n, 0] - mu) <= 3e-5 * magm + 1e-6).all()
+            assert (np.abs(gstat[b, h * G + g, :n, 1] - s2) <= 1e-4 * s2 + 1e-6).all()
+
+
+@pytest.mark.parametrize("name", ["needle4k_f32_d64", "needle32k_gqa", "cluster_p64"])
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_topk_decode(gpu, name, alpha):
+    inp, host = inputs(name, gpu)
+    spec = inp.spec
+    k = spec.topk or 32
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_topk(inp.q, alpha, k)
+    torch.cuda.synchronize()
+    sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
+    tau, out = f64(buf.tau), f64(buf.out)
+    P, G, sc = spec.page_size, spec.group, scale_of(spec)
+    swaps = 0
+    for b, h in _units(inp):
+        qs, keys, vals = host.unit(b, h)
+        kmin, kmax, _, _ = O.unit_metadata(keys, P)
+        g = np.max([O.bbox_bound(qs[j], kmin, kmax, sc) for j in range(G)], axis=0)
+        got = sel[b, h, :cnt[b, h]]
+        assert (np.diff(got) > 0).all()
+        swaps += check_topk_selection(got, g, k)
+        ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
+        for j in range(G):
+            hq = h * G + j
+            assert abs(tau[b, hq] - ref["tau"][j]) <= TAU_ATOL
+            assert rel_l2(out[b, hq], ref["out"][j]) <= OUT_RTOL_L2
+    print("near-cutoff swaps:", swaps)
+
+
+@pytest.mark.parametrize("name", ["cluster_b2_ragged", "cluster_p64", "pool_permuted", "needle32k_gqa"])
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_gauss_decode(gpu, name, alpha):
+    inp, host = inputs(name, gpu)
+    spec = inp.spec
+    delta = spec.delta
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_gauss(inp.q, alpha, delta)
+    torch.cuda.synchronize()
+    sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
+    tau_hat, tau, out = f64(buf.tau_hat), f64(buf.tau), f64(buf.out)
+    P, G, sc = spec.page_size, spec.group, scale_of(spec)
+    for b, h in _units(inp):
+        qs, keys, vals = host.unit(b, h)
+        _, _, mean, var = O.unit_metadata(keys, P)
+        n_tok = O.page_token_counts(keys.shape[0], P)
+        mu, s2 = zip(*[O.gauss_moments(qs[j], mean, var, sc) for j in range(G)])
+        mu, s2 = np.stack(mu), np.stack(s2)
+        th = np.array([O.solve_tau_hat(mu[j], s2[j], n_tok, alpha) for j in range(G)])
+        for j in range(G):
+            assert abs(tau_hat[b, h * G + j] - th[j]) <= TAU_ATOL, (b, h, j)
+        got = sel[b, h, :cnt[b, h]]
+        assert cnt[b, h] >= 1 and (np.diff(got) > 0).all()
+        check_gauss_selection(got, mu, s2, n_tok, th, alpha, delta)
+        ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
+        for j in range(G):
+            hq = h * G + j
+            assert abs(tau[b, hq] - ref["tau"][j]) <= TAU_ATOL
+            assert rel_l2(out[b, hq], ref["out"][j]) <= OUT_RTOL_L2
+
+
+@pytest.mark.parametrize("name", ["needle4k_f32_d64", "cluster_b2_ragged", "pool_permuted"])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_full_cache_entmax(gpu, name, alpha):
+    inp, host = inputs(name, gpu)
+    spec = inp.spec
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    probs = torch.full((spec.batch, spec.num_q_heads, inp.max_pages * spec.page_size),
+                       -1.0, device=gpu)
+    buf.entmax(inp.q, alpha, selected=False, probs=probs)
+    torch.cuda.synchronize()
+    tau, out, pr = f64(buf.tau), f64(buf.out), f64(probs)
+    G, sc = spec.group, scale_of(spec)
+    for b, h in _units(inp):
+        qs, keys, vals = host.unit(b, h)
+        N = keys.shape[0]
+        for j in range(G):
+            hq = h * G + j
+            z = (alpha - 1) * O.token_scores(qs[j], keys, sc)
+            t = O.entmax_threshold(z, alpha)
+            p = O.entmax_probs(z, t, alpha)
+            o = (p[:, None] * vals).sum(0)
+            assert abs(tau[b, hq] - t) <= TAU_ATOL
+            assert rel_l2(out[b, hq], o) <= OUT_RTOL_L2
+            pg = pr[b, hq, :N]
+            assert (pg >= 0).all() and abs(pg.sum() - 1) < 1e-4
+            assert np.abs(pg - p).max() < 1e-4
+
+
+@pytest.mark.parametrize("name", ["needle4k_f32_d64", "needle32k_gqa", "cluster_b2_ragged", "pool_permuted"])
+def test_full_cache_softmax(gpu, name):
+    inp, host = inputs(name, gpu)
+    spec = inp.spec
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv, softmax=True)
+    buf.softmax(inp.q)
+    torch.cuda.synchronize()
+    out, lse = f64(buf.out), f64(buf.lse)
+    G, sc = spec.group, scale_of(spec)
+    for b, h in _units(inp):
+        qs, keys, vals = host.unit(b, h)
+        for j in range(G):
+            o, l = O.softmax_attend(qs[j], keys, vals, sc)
+            assert rel_l2(out[b, h * G + j], o) <= OUT_RTOL_L2
+            assert abs(lse[b, h * G + j] - l) <= 1e-4 * max(1, abs(l))
+
+
+def test_selection_covering_support_matches_full_cache(gpu):
+    # Technical Summary, §3: when the kept pages contain the support the sparse
+    # output is the full-cache output.  Top-k with k >= n_pages keeps all.
+    inp, host = inputs("cluster_b2_ragged", gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_topk(inp.q, 1.5, inp.max_pages)
+    torch.cuda.synchronize()
+    sparse = (buf.out.clone(), buf.tau.clone())
+    buf.entmax(inp.q, 1.5, selected=False)
+    torch.cuda.synchronize()
+    assert torch.equal(sparse[1], buf.tau)
+    assert torch.equal(sparse[0], buf.out)
+    buf.step_gauss(inp.q, 1.5, math.inf)
+    torch.cuda.synchronize()
+    P = inp.spec.page_size
+    for b in range(inp.spec.batch):
+        assert (buf.count[b] == (inp.lens[b] + P - 1) // P).all()
+    assert torch.equal(sparse[0], buf.out)
+
+
+def test_determinism_and_slot_permutation(gpu):
+    inp, host = inputs("pool_permuted", gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    res = []
+    for _ in range(2):
+        buf.step_gauss(inp.q, 1.5, 0.5)
+        torch.cuda.synchronize()
+        res.append((buf.sel.clone(), buf.count.clone(), buf.tau_hat.clone(),
+                    buf.tau.clone(), buf.out.clone()))
+    for a, b_ in zip(*res):
+        assert torch.equal(a, b_)
+    # move every page to another slot: results must not change
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(3)
+    perm = torch.randperm(inp.num_slots, generator=gen).to(gpu)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(inp.num_slots, device=gpu)
+    k2 = torch.empty_like(inp.k)
+    v2 = torch.empty_like(inp.v)
+    k2[perm] = inp.k
+    v2[perm] = inp.v
+    pt2 = perm[inp.page_table.long()].to(torch.int32)
+    kv2 = ekv.PagedKV(k2, v2, pt2, inp.seq_lens, inp.spec.group)
+    buf2 = ekv.DecodeBuffers(kv2)
+    buf2.build_meta()
+    buf2.step_gauss(inp.q, 1.5, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(buf2.count, res[0][1])
+    assert torch.equal(buf2.tau_hat, res[0][2])
+    assert torch.equal(buf2.out, res[0][4])
+
+
+def test_edge_cases(gpu):
+    # one-token sequence, a sequence ending one token into a page, and the
+    # Gaussian selector's empty-set fallback on identical pages.
+    spec = workloads.workload("needle_32k_gqa", batch=1, seq_len=1, needles=0)
+    print("[case] single-token sequence", flush=True)
+    inp = workloads.generate(spec, 106, gpu)
+    host = HostCopy(inp)
+    buf = ekv.DecodeBuffers(paged_kv(inp))
+    buf.build_meta()
+    buf.step_topk(inp.q, 1.5, 4)
+    torch.cuda.synchronize()
+    assert (buf.count == 1).all()
+    v = f64(inp.v)
+    for h in range(spec.num_kv_heads):
+        for j in range(spec.group):
+            np.testing.assert_allclose(f64(buf.out)[0, h * spec.group + j],
+                                       v[host.pt[0, 0], h, 0], rtol=1e-6)
+
+    # identical pages: every page has the same Gaussian, the threshold
+    # estimate sits above every page's estimated maximum with delta = 0.
+    D, P, npg = 128, 64, 512
+    print("[case] identical pages fallback", flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    page = torch.randn(P, D, generator=g)
+    k = page.repeat(npg, 1, 1).reshape(npg, 1, P, D).to(torch.bfloat16).to(gpu)
+    vv = torch.randn(npg, 1, P, D, generator=g).to(torch.bfloat16).to(gpu)
+    pt = torch.arange(npg, dtype=torch.int32, device=gpu).reshape(1, npg)
+    sl = torch.tensor([npg * P], dtype=torch.int32, device=gpu)
+    q = torch.randn(1, 1, D, generator=g).to(gpu)
+    kv = ekv.PagedKV(k, vv, pt, sl, 1)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_gauss(q, 1.5, 0.0)
+    torch.cuda.synchronize()
+    # oracle side, from the keys: every page holds the same 64 keys
+    keys_page = f64(k[0, 0])
+    _, _, mean, var = O.page_metadata(keys_page)
+    mu, s2 = O.gauss_moments(f64(q)[0, 0], mean[None], var[None], 1 / math.sqrt(D))
+    n_tok = np.full(npg, P)
+    mu, s2 = np.full(npg, mu[0]), np.full(npg, s2[0])
+    th = O.solve_tau_hat(mu, s2, n_tok, 1.5)
+    kept = O.gauss_keep(mu[None], s2[None], n_tok, np.array([th]), 1.5, 0.0)
+    assert list(kept) == [0]  # the empty-set fallback is what is exercised
+    assert abs(f64(buf.tau_hat)[0, 0] - th) <= TAU_ATOL
+    assert int(buf.count[0, 0]) == 1
+    assert int(buf.sel[0, 0, 0]) == 0
