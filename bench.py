@@ -5,8 +5,9 @@ One step = one decode step for every (sequence, KV head) of the workload:
 refresh of each sequence's tail-page metadata, Gaussian page scoring,
 Gaussian-aware selection, gathered entmax attention (scores, threshold,
 apply).  The headline value is decode tokens/s = batch / median step time,
-with the inputs resident in HBM and the caches flushed (a 512 MiB write)
-between steps, outside the timed events.  Beside it the top-k path and the
+with the inputs resident in HBM and the caches flushed between steps
+(a 1 GiB read, so that no dirty lines are left to write back), outside the
+timed events.  Beside it the top-k path and the
 full-cache entmax and split-K softmax baselines are timed the same way.
 
 Each kernel of a step is bracketed by HIP events on the stream the library
@@ -38,7 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cluster_1m")
     ap.add_argument("--seed", type=int, default=3000)
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="cache flush between timed steps (outside the events): "
+                         "read a 1 GiB buffer (default), write 512 MiB, or none")
     ap.add_argument("--cpu-units", type=int, default=1,
                     help="(sequence, KV head) units the oracle is timed on; 0 skips")
     ap.add_argument("--legs", default="gauss,topk,entmax_full,softmax_full")
@@ -78,7 +81,28 @@ def main():
     delta = spec.delta
     q = inp.q
     tail = torch.tensor([(L - 1) // P for L in inp.lens], dtype=torch.int32, device=dev)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    if args.flush == "read":
+        flush_buf = torch.ones(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
+        flush = lambda s: torch.amax(flush_buf)
+    elif args.flush == "write":
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush = lambda s: flush_buf.fill_(s & 0xFF)
+    else:
+        flush = None
+
+    # Measured HBM read ceiling: the library's streaming-read probe over
+    # 2 GiB (well beyond the 256 MB last-level cache), median of 5.
+    probe = torch.ones(512 << 20, dtype=torch.float32, device=dev)
+    sink = torch.empty(ekv.EKV_READ_PROBE_SINK, dtype=torch.int32, device=dev)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
+    for i in range(6):
+        pe[2 * i].record(stream)
+        ekv.ekv_read_probe(probe, sink)
+        pe[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    probe_ms = statistics.median(pe[2 * i].elapsed_time(pe[2 * i + 1]) for i in range(1, 6))
+    read_probe_gbps = probe.numel() * 4 / (probe_ms * 1e-3) / 1e9
+    del probe, sink
 
     # Full metadata build (once; timed on its own).
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -139,7 +163,7 @@ def main():
         t_start = time.perf_counter()
         for s in range(steps):
             if flush is not None:
-                flush.fill_(s & 0xFF)
+                flush(s)
             evs[s][0].record(stream)
             for i, (_, fn) in enumerate(phases):
                 fn()
@@ -263,13 +287,14 @@ def main():
                    "kv_heads": H, "group": G, "head_dim": D, "page_size": P,
                    "kv_dtype": spec.kv_dtype, "alpha": alpha, "selector": head_name,
                    "delta": delta, "topk": k_top, "parallelism": "single GPU",
-                   "cache_flush_between_steps": flush is not None},
+                   "cache_flush_between_steps": args.flush},
         "hbm_gbps": round(head["hbm_gbps"], 1),
         "hbm_frac_of_peak": round(head["hbm_gbps"] / PEAK_HBM_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "speedups": speedups,
         "meta_build_ms": round(meta_build_ms, 4),
+        "hbm_read_probe_gbps": round(read_probe_gbps, 1),
         "legs": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                      for kk, vv in v.items()} for k, v in results.items()},
     }

@@ -134,12 +134,21 @@ ekv_status ekv_build_meta(const ekv_paged_kv *kv, const int32_t *first_page,
  * ekv_score_pages - query-aware page scoring (Technical Summary, §2.A).
  *   q      [batch][H_q][head_dim] float32, H_q = num_kv_heads * group.
  *   mode   EKV_SCORE_BBOX and/or EKV_SCORE_GAUSS.
- *   ub     [batch][H_q][max_pages] float32 (BBOX): the box upper bound
- *          scale * sum_d max(q_d kmin_d, q_d kmax_d) of every page's scores.
- *   gstat  [batch][H_q][max_pages][2] float32 (GAUSS): mean
- *          scale * <q, mean> and variance scale^2 * sum_d q_d^2 var_d of a
- *          page key's score under the page's diagonal Gaussian.
- * Columns >= ceil(seq_lens[b]/P) are left untouched.
+ *   ub     (BBOX) ekv_score_size(kv, EKV_SCORE_BBOX) floats:
+ *          [batch][H_q][max_pages] the box upper bound
+ *          scale * sum_d max(q_d kmin_d, q_d kmax_d) of every page's scores,
+ *          followed by [batch][num_kv_heads][T] the largest bound over each
+ *          tile of 64 logical pages and the group's query heads
+ *          (T = ceil(max_pages / 64)).
+ *   gstat  (GAUSS) ekv_score_size(kv, EKV_SCORE_GAUSS) floats:
+ *          [batch][H_q][max_pages][2] the mean scale * <q, mean> and the
+ *          variance scale^2 * sum_d q_d^2 var_d of a page key's score under
+ *          the page's diagonal Gaussian, followed (from the next multiple of
+ *          4 floats) by [batch][H_q][T][4] per 64-page tile: max mu,
+ *          max (mu + 8.5 sigma), max (mu + sqrt(2 ln P) sigma), 0.
+ * The tile summaries let the selectors skip tiles that cannot matter.
+ * Columns >= ceil(seq_lens[b]/P), and tiles past the last page, are left
+ * untouched.  gstat must be 16-byte aligned.
  */
 ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
                            const float *q, float scale, int32_t mode,
@@ -238,6 +247,21 @@ ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
                               float scale, const int32_t *sel,
                               const int32_t *count, float *out, float *lse,
                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ekv_read_probe - measurement aid (not part of the method): streams `bytes`
+ * (a multiple of 16, buf 16-byte aligned) from the device buffer `buf` with
+ * 16-byte loads over the whole device and writes one 32-bit checksum per
+ * wave to sink[0 .. EKV_READ_PROBE_SINK).  Timing it gives the HBM read
+ * bandwidth the decode kernels' load pattern can reach.
+ */
+#define EKV_READ_PROBE_SINK 8192
+ekv_status ekv_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                          void *stream);
+
+/* Floats of the ub (EKV_SCORE_BBOX) or gstat (EKV_SCORE_GAUSS) buffer,
+ * page values plus tile summaries (host only; 0 on invalid input). */
+size_t ekv_score_size(const ekv_paged_kv *kv, int32_t mode);
 
 /* Bytes of workspace an operation needs (host only; 0 on invalid input). */
 size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0);

@@ -79,6 +79,8 @@ _SIGNATURES = {
                                     _c_p]),
     "ekv_workspace_size": (_c_size, [_c_i32, ctypes.POINTER(ekv_paged_kv),
                                      _c_i32]),
+    "ekv_read_probe": (_c_i32, [_c_p, _c_size, _c_p, _c_p]),
+    "ekv_score_size": (_c_size, [ctypes.POINTER(ekv_paged_kv), _c_i32]),
     "ekv_status_string": (ctypes.c_char_p, [_c_i32]),
     "ekv_last_error": (ctypes.c_char_p, []),
     "ekv_version": (_c_i32, []),
@@ -189,6 +191,11 @@ def ekv_workspace_size(op: int, kv: PagedKV, k: int = 0) -> int:
     return int(load_library().ekv_workspace_size(op, ctypes.byref(s), k))
 
 
+def ekv_score_size(kv: PagedKV, mode: int) -> int:
+    s = kv.struct()
+    return int(load_library().ekv_score_size(ctypes.byref(s), mode))
+
+
 def ekv_build_meta(kv: PagedKV, bbox, gauss, first_page=None, span_hint=0,
                    stream=None) -> None:
     s, m = kv.struct(), _meta(bbox, gauss)
@@ -267,6 +274,16 @@ def ekv_softmax_decode(kv: PagedKV, q, scale: float, sel, count, out,
         ctypes.byref(s), _ptr(q), float(scale), _ptr(sel), _ptr(count),
         _ptr(out), _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)), "ekv_softmax_decode")
+
+
+EKV_READ_PROBE_SINK = 8192
+
+
+def ekv_read_probe(buf, sink, stream=None) -> None:
+    """Stream all of ``buf`` (bytes a multiple of 16) through the read probe."""
+    _check(load_library().ekv_read_probe(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+        _stream(stream)), "ekv_read_probe")
 
 
 def ekv_version() -> int:

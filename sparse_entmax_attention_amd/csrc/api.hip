@@ -56,6 +56,8 @@ ekv_status check_kv(const ekv_paged_kv *kv, bool need_k, bool need_v) {
   if (kv->group != 1 && kv->group != 2 && kv->group != 4 && kv->group != 8)
     return fail(EKV_ERR_UNSUPPORTED, "group %d (built: 1, 2, 4, 8)",
                 kv->group);
+  if (static_cast<long long>(kv->batch) * kv->num_kv_heads > 4096)
+    return fail(EKV_ERR_UNSUPPORTED, "batch * num_kv_heads exceeds 4096");
   const double cells = static_cast<double>(kv->max_pages) * kv->page_size;
   if (cells > 2147483647.0)
     return fail(EKV_ERR_UNSUPPORTED, "max_pages * page_size exceeds 2^31-1");
@@ -148,8 +150,9 @@ size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
   if (check_kv(kv, false, false) != EKV_OK) return 0;
   const size_t units = static_cast<size_t>(kv->batch) * kv->num_kv_heads;
   switch (op) {
-    case EKV_OP_SELECT_TOPK:
-      return ((units * kv->max_pages * 4) + 255) & ~static_cast<size_t>(255);
+    case EKV_OP_SELECT_TOPK:  // candidate keys, whole tiles of pages
+      return ((units * ekv::page_tiles(*kv) * ekv::kPageTile * 4) + 255) &
+             ~static_cast<size_t>(255);
     case EKV_OP_SELECT_GAUSS:
       return 0;
     case EKV_OP_ENTMAX_DECODE:
@@ -159,6 +162,18 @@ size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
     default:
       return 0;
   }
+}
+
+size_t ekv_score_size(const ekv_paged_kv *kv, int32_t mode) {
+  if (check_kv(kv, false, false) != EKV_OK) return 0;
+  const size_t Hq = static_cast<size_t>(kv->num_kv_heads) * kv->group;
+  const size_t B = kv->batch, H = kv->num_kv_heads, MP = kv->max_pages;
+  const size_t T = ekv::page_tiles(*kv);
+  if (mode == EKV_SCORE_BBOX) return B * Hq * MP + B * H * T;
+  if (mode == EKV_SCORE_GAUSS)
+    return ekv::gstat_tile_offset(kv->batch, static_cast<int>(Hq), kv->max_pages) +
+           B * Hq * T * 4;
+  return 0;
 }
 
 ekv_status ekv_build_meta(const ekv_paged_kv *kv, const int32_t *first_page,
@@ -192,8 +207,8 @@ ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
     return fail(EKV_ERR_INVALID_ARG, "Gaussian scoring needs meta->gauss and gstat");
   if ((meta->bbox && !aligned(meta->bbox, 16)) ||
       (meta->gauss && !aligned(meta->gauss, 16)) || !aligned(q, 16) ||
-      (gstat && !aligned(gstat, 8)))
-    return fail(EKV_ERR_INVALID_ARG, "q/metadata must be 16-byte aligned, gstat 8");
+      (gstat && !aligned(gstat, 16)))
+    return fail(EKV_ERR_INVALID_ARG, "q, metadata and gstat must be 16-byte aligned");
   const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
     return ekv::launch_score<decltype(E), decltype(D)::value,
                              decltype(G)::value>(*kv, *meta, q, scale, mode,
@@ -232,7 +247,7 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
                 static_cast<double>(delta));
   if (!gstat || !sel || !count || !tau_hat)
     return fail(EKV_ERR_INVALID_ARG, "gstat, sel, count and tau_hat are required");
-  if (!aligned(gstat, 8)) return fail(EKV_ERR_INVALID_ARG, "gstat must be 8-byte aligned");
+  if (!aligned(gstat, 16)) return fail(EKV_ERR_INVALID_ARG, "gstat must be 16-byte aligned");
   EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0)));
   const hipError_t e = with_g(*kv, [&](auto G) {
     return ekv::launch_select_gauss<decltype(G)::value>(
@@ -321,6 +336,15 @@ ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
                                                    as_stream(stream));
   });
   return hip_status(e, "ekv_softmax_decode launch");
+}
+
+ekv_status ekv_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                          void *stream) {
+  if (!buf || !sink || !aligned(buf, 16) || (bytes & 15) != 0)
+    return fail(EKV_ERR_INVALID_ARG,
+                "buf (16-byte aligned), sink and a multiple of 16 bytes required");
+  return hip_status(ekv::launch_read_probe(buf, bytes, sink, as_stream(stream)),
+                    "ekv_read_probe launch");
 }
 
 const char *ekv_status_string(ekv_status s) {

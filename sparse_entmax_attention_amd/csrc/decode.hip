@@ -3,17 +3,18 @@
 // §4 "Efficiency").
 //
 // Entmax has no single-pass running form: the threshold tau depends on every
-// score.  The step is therefore split in three launches over "chunks" of
-// kChunkTokens token positions of a unit's selected pages:
-//   1. scores:    gather K, z = (alpha-1) scale <q, k> for the G query heads,
-//                 write z (float32) and each chunk's maximum;
-//   2. threshold: per query head, tau from the z of the chunks whose maximum
-//                 exceeds max z - 1 (tau >= max z - 1, so no other token can
-//                 have p > 0); exact for alpha in {1.5, 2};
-//   3. apply:     p = max(z - tau, 0)^r; V rows are read only where some head
-//                 has p > 0 (exact: the other rows carry zero weight), chunk
-//                 partials are merged in chunk order.
-// Reads: selected K once, V only on the support, z twice (from cache).
+// score.  The step is therefore split in three launches:
+//   1. scores:    one wave per selected page gathers its keys and computes
+//                 z = (alpha-1) scale <q, k> for the G query heads on the
+//                 matrix cores; z and each page's maximum are written;
+//   2. threshold: per query head, tau from the tokens that can still be in
+//                 the support (tau is at least max z - 1, and at least
+//                 c - k^-(alpha-1) whenever k page maxima reach c); exact
+//                 for alpha in {1.5, 2};
+//   3. apply:     per chunk of pages, p = max(z - tau, 0)^r and value rows
+//                 are read only where some head has p > 0 (the other rows
+//                 carry zero weight); chunk partials are merged in order.
+// HBM reads: selected K once, V only on the support, z twice.
 #include <float.h>
 
 #include "ekv_device.h"
@@ -24,6 +25,10 @@ namespace ekv {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kMaxChunkPages = kChunkTokens / 16;  // smallest page size
+constexpr int kMaxUnits = 4096;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   const size_t units = static_cast<size_t>(kv.batch) * kv.num_kv_heads;
@@ -33,8 +38,8 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   DecodeWs w;
   w.z = 0;
-  w.cmax = al(w.z + units * G * cap * 4);
-  w.tau = al(w.cmax + units * G * mc * 4);
+  w.cmax = al(w.z + units * G * cap * 4);  // per-page maxima
+  w.tau = al(w.cmax + units * G * static_cast<size_t>(kv.max_pages) * 4);
   w.part_o = al(w.tau + units * G * 4);
   w.part_s = al(w.part_o + units * mc * G * D * 4);
   w.total = al(w.part_s + units * mc * G * 4);
@@ -54,35 +59,68 @@ SoftmaxWs softmax_ws_layout(const ekv_paged_kv &kv) {
   return w;
 }
 
-// Pages of one chunk, staged in LDS: logical page, slot, valid tokens.
-struct ChunkPages {
-  int lp[kMaxChunkPages];
-  int slot[kMaxChunkPages];
-  int nt[kMaxChunkPages];
+// ---------------------------------------------------------------------------
+// Work lists.  Work items (pages or chunks of pages) of all units are laid
+// end to end, unit by unit; a persistent grid walks them with a stride.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int unit_pages(const int32_t *seq_lens,
+                                          const int32_t *sel,
+                                          const int32_t *count, int u, int H,
+                                          int P) {
+  return sel ? count[u] : n_pages_of(seq_lens[u / H], P);
+}
+
+// pref[u] = first item of unit u (pref[units] = total); returns the total.
+template <int NT>
+__device__ int build_unit_prefix(int *pref, int *tmp, const int32_t *seq_lens,
+                                 const int32_t *sel, const int32_t *count,
+                                 int units, int H, int P, int pages_per_item) {
+  const int per = (units + NT - 1) / NT;
+  const int u0 = threadIdx.x * per, u1 = min(units, u0 + per);
+  int local = 0;
+  for (int u = u0; u < u1; ++u)
+    local += (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
+             pages_per_item;
+  int total;
+  int base = block_excl_scan<NT>(local, tmp, total);
+  for (int u = u0; u < u1; ++u) {
+    pref[u] = base;
+    base += (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
+            pages_per_item;
+  }
+  if (threadIdx.x == 0) pref[units] = total;
+  lds_barrier();
+  return total;
+}
+
+// Largest u with pref[u] <= f.
+__device__ __forceinline__ int find_unit(const int *pref, int units, int f) {
+  int lo = 0, hi = units - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pref[mid] <= f) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Location of a selected page.
+struct PageRef {
+  int u, j, lp, slot, nt;
 };
 
-// Returns false (uniformly for the block) when chunk c is past the unit's
-// selection.  Otherwise fills `cp` and sets j0/j1 (selection entries).
-__device__ __forceinline__ bool stage_chunk(
-    ChunkPages &cp, const int32_t *page_table, const int32_t *seq_lens,
-    const int32_t *sel, const int32_t *count, int u, int H, int P,
-    int max_pages, int c, int &j0, int &j1, int &len) {
-  const int b = u / H;
-  len = seq_lens[b];
-  const int cnt = sel ? count[u] : n_pages_of(len, P);
-  const int ppc = kChunkTokens / P;
-  j0 = c * ppc;
-  if (j0 >= cnt) return false;
-  j1 = min(cnt, j0 + ppc);
-  if (threadIdx.x < j1 - j0) {
-    const int j = j0 + threadIdx.x;
-    const int lp = sel ? sel[static_cast<size_t>(u) * max_pages + j] : j;
-    cp.lp[threadIdx.x] = lp;
-    cp.slot[threadIdx.x] = page_table[static_cast<size_t>(b) * max_pages + lp];
-    cp.nt[threadIdx.x] = page_tokens(lp, len, P);
-  }
-  __syncthreads();
-  return true;
+__device__ __forceinline__ PageRef page_ref(const int *pref, int units, int f,
+                                            const int32_t *page_table,
+                                            const int32_t *seq_lens,
+                                            const int32_t *sel, int H, int P,
+                                            int max_pages) {
+  PageRef r;
+  r.u = find_unit(pref, units, f);
+  r.j = f - pref[r.u];
+  const int b = r.u / H;
+  r.lp = sel ? sel[static_cast<size_t>(r.u) * max_pages + r.j] : r.j;
+  r.slot = page_table[static_cast<size_t>(b) * max_pages + r.lp];
+  r.nt = page_tokens(r.lp, seq_lens[b], P);
+  return r;
 }
 
 __device__ __forceinline__ float pow_r(float x, int r, float rg) {
@@ -93,124 +131,234 @@ __device__ __forceinline__ float pow_r(float x, int r, float rg) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Scores.  D/8 lanes per token (16-byte K loads), U tokens per lane in
-// flight per step.
+// 1a. Scores on the matrix cores (bfloat16 keys).
+//
+// v_mfma_f32_16x16x32_bf16 multiplies a 16x32 A by a 32x16 B.  B holds 16
+// tokens' keys for 32 coordinates: lane l supplies 8 consecutive
+// coordinates (one 16-byte load) of token l%16, block l/16.  A holds the
+// query: row 4*s + g is the s-th bfloat16 part of (alpha-1)*scale*q_g, where
+// q = part0 + part1 + part2 to float32 precision (each part is the bfloat16
+// rounding of what the previous parts left over); rows 12..15 are zero.
+// Products of bfloat16 values are exact and accumulate in float32, so
+// summing the three row results gives z to float32 accuracy.  Output lane l
+// holds rows 4*(l/16) + i of column l%16, i.e. part l/16 of head i.
 // ---------------------------------------------------------------------------
-constexpr int kUnroll = 4;
+__device__ __forceinline__ int kb_of(int lane) { return lane >> 4; }
 
+__device__ __forceinline__ float bf16_part(float x, int part) {
+  const float p0 = static_cast<float>(static_cast<__bf16>(x));
+  const float r1 = x - p0;
+  const float p1 = static_cast<float>(static_cast<__bf16>(r1));
+  const float r2 = r1 - p1;
+  const float p2 = static_cast<float>(static_cast<__bf16>(r2));
+  return part == 0 ? p0 : part == 1 ? p1 : p2;
+}
+
+template <int D, int G>
+__device__ __forceinline__ void load_q_parts(bf16x8_t (&a)[(G + 3) / 4][D / 32],
+                                             const float *q, int b, int h,
+                                             int H, float zscale) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, kb = lane >> 4;
+  const int Hq = H * G;
+#pragma unroll
+  for (int ps = 0; ps < (G + 3) / 4; ++ps) {
+    const int part = n >> 2, g = (n & 3) + 4 * ps;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = 0.f;
+        if (part < 3 && g < G)
+          x = bf16_part(q[(static_cast<size_t>(b) * Hq + h * G + g) * D +
+                          32 * s + 8 * kb + i] * zscale, part);
+        a[ps][s][i] = static_cast<__bf16>(x);
+      }
+  }
+}
+
+template <int D, int G, int P>
+__global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
+    const uint16_t *__restrict__ kpool, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
+    const int32_t *__restrict__ count, const float *__restrict__ q,
+    float zscale, int units, int H, int max_pages, int cap,
+    float *__restrict__ zbuf, float *__restrict__ pmax) {
+  constexpr int KS = D / 32;            // k-steps of 32 coordinates
+  constexpr int NPASS = (G + 3) / 4;    // groups of 4 query heads
+  constexpr int NT16 = P / 16;          // 16-token groups per page
+  __shared__ int pref[kMaxUnits + 1];
+  __shared__ int tmp[kDecWaves];
+  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
+                                                   count, units, H, P, 1);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15, kb = lane >> 4;
+  const int nwaves = gridDim.x * kDecWaves;
+
+  bf16x8_t a[NPASS][KS];
+  int cur_u = -1;
+  int f = blockIdx.x * kDecWaves + wave;
+  if (f >= total) return;
+  PageRef cur = page_ref(pref, units, f, page_table, seq_lens, sel, H, P,
+                         max_pages);
+  while (true) {
+    const int fn = f + nwaves;
+    PageRef nxt = cur;
+    if (fn < total)
+      nxt = page_ref(pref, units, fn, page_table, seq_lens, sel, H, P,
+                     max_pages);
+    const int u = cur.u, h = u % H, b = u / H;
+    if (u != cur_u) {
+      cur_u = u;
+      load_q_parts<D, G>(a, q, b, h, H, zscale);
+    }
+    const uint16_t *base = kpool + pool_row(cur.slot, h, 0, H, P, D);
+    bf16x8_t bv[NT16][KS];
+#pragma unroll
+    for (int t = 0; t < NT16; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        bv[t][s] = *reinterpret_cast<const bf16x8_t *>(
+            base + static_cast<size_t>(16 * t + n) * D + 32 * s + 8 * kb);
+    float *zu = zbuf + static_cast<size_t>(u) * G * cap +
+                static_cast<size_t>(cur.j) * P;
+    float pm[NPASS][4];
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pm[ps][i] = -FLT_MAX;
+#pragma unroll
+    for (int t = 0; t < NT16; ++t) {
+      const bool valid = 16 * t + n < cur.nt;
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], bv[t][s], c,
+                                                      0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p1 = __shfl_down(c[i], 16, kWave);
+          const float p2 = __shfl_down(c[i], 32, kWave);
+          const float z = c[i] + (p1 + p2);
+          const int g = 4 * ps + i;
+          if (g < G && lane < 16) {
+            zu[static_cast<size_t>(g) * cap + 16 * t + n] = valid ? z : -INFINITY;
+            if (valid) pm[ps][i] = fmaxf(pm[ps][i], z);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * ps + i;
+        if (g < G) {
+          const float m = group_max<16>(pm[ps][i]);
+          if (lane == 0)
+            pmax[(static_cast<size_t>(u) * G + g) * max_pages + cur.j] = m;
+        }
+      }
+    if (fn >= total) break;
+    f = fn;
+    cur = nxt;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1b. Scores on the vector units (float32 keys).  One wave per page; D/8
+// lanes per token, 8 coordinates per lane.
+// ---------------------------------------------------------------------------
 template <class E, int D, int G>
-__global__ __launch_bounds__(kDecThreads) void k_entmax_scores(
+__global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
     const typename E::T *__restrict__ kpool,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
-    float zscale, int H, int P, int max_pages, int cap, int maxch,
-    float *__restrict__ zbuf, float *__restrict__ cmax) {
+    float zscale, int units, int H, int P, int max_pages, int cap,
+    float *__restrict__ zbuf, float *__restrict__ pmax) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
-  constexpr int STEP = kDecWaves * TPW * kUnroll;  // tokens per block step
-  static_assert(kChunkTokens % STEP == 0, "chunk must be whole steps");
-  __shared__ ChunkPages cp;
-  __shared__ float red[kDecWaves][G];
-  const int u = blockIdx.y, c = blockIdx.x;
-  const int h = u % H, b = u / H;
-  int j0, j1, len;
-  if (!stage_chunk(cp, page_table, seq_lens, sel, count, u, H, P, max_pages,
-                   c, j0, j1, len))
-    return;
+  __shared__ int pref[kMaxUnits + 1];
+  __shared__ int tmp[kDecWaves];
+  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
+                                                   count, units, H, P, 1);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
   const int Hq = H * G;
-
-  float qs[G][8];
+  const int nwaves = gridDim.x * kDecWaves;
+  for (int f = blockIdx.x * kDecWaves + wave; f < total; f += nwaves) {
+    const PageRef r = page_ref(pref, units, f, page_table, seq_lens, sel, H, P,
+                               max_pages);
+    const int u = r.u, h = u % H, b = u / H;
+    float qs[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float *qg = q + (static_cast<size_t>(b) * Hq + h * G + g) * D + d0;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qs[g][j] = qg[j] * zscale;
-  }
-  float mx[G];
+      for (int j = 0; j < 8; ++j)
+        qs[g][j] = q[(static_cast<size_t>(b) * Hq + h * G + g) * D + d0 + j] * zscale;
+    float mx[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -FLT_MAX;
-  const int npos = (j1 - j0) * P;
-  float *zu = zbuf + static_cast<size_t>(u) * G * cap;
-
-  for (int base = 0; base < kChunkTokens; base += STEP) {
-    float x[kUnroll][8];
-    bool valid[kUnroll];
-    int pos[kUnroll];
-#pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-      const int i = base + (r * kDecWaves + wave) * TPW + sub;
-      const int jj = i / P, t = i - jj * P;
-      pos[r] = i;
-      valid[r] = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-      if (valid[r]) {
-        load8(kpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x[r]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[r][j] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-      float acc[G];
+    for (int g = 0; g < G; ++g) mx[g] = -FLT_MAX;
+    float *zu = zbuf + static_cast<size_t>(u) * G * cap +
+                static_cast<size_t>(r.j) * P;
+    for (int t0 = 0; t0 < P; t0 += TPW) {
+      const int t = t0 + sub;
+      float x[8];
+      load8(kpool + pool_row(r.slot, h, t, H, P, D) + d0, x);
+      const bool valid = t < r.nt;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[r][j], a);
-        acc[g] = group_sum<LPT>(a);
-      }
-      if (pos[r] < npos) {
-        const size_t zi = static_cast<size_t>(j0) * P + pos[r];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float z = valid[r] ? acc[g] : -INFINITY;
-          if (li == g) zu[static_cast<size_t>(g) * cap + zi] = z;
-          if (valid[r]) mx[g] = fmaxf(mx[g], acc[g]);
-        }
+        for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[j], a);
+        a = group_sum<LPT>(a);
+        if (li == g) zu[static_cast<size_t>(g) * cap + t] = valid ? a : -INFINITY;
+        if (valid) mx[g] = fmaxf(mx[g], a);
       }
     }
-  }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = group_max<kWave>(mx[g]);
-    if (lane == 0) red[wave][g] = m;
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float m = red[0][threadIdx.x];
-#pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, red[w][threadIdx.x]);
-    cmax[(static_cast<size_t>(u) * G + threadIdx.x) * maxch + c] = m;
+    for (int g = 0; g < G; ++g) {
+      const float m = group_max<kWave>(mx[g]);
+      if (lane == 0) pmax[(static_cast<size_t>(u) * G + g) * max_pages + r.j] = m;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. Threshold.  One block per query head.
 //
-// With M = max z and L = M - 1, tau lies in [L, M).  The candidates z > L are
-// counted into kTauBins equal bins of [L, M].  For the bin edge e_b, token
-// values z in bin c >= b satisfy (c-b)/NB <= z - e_b < (c+1-b)/NB, so
-//   F_lo(b) = sum_{c>=b} cnt_c ((c-b)/NB)^r  <=  F(e_b)  <=  F_hi(b) = ...(c+1-b)
-// with F(t) = sum_i max(z_i - t, 0)^r; for r in {1, 2} both are polynomials in
-// b of suffix sums of cnt_c c^k, exact in double.  The largest b with
-// F_lo >= 1 and the smallest with F_hi < 1 bracket tau.  Tokens above the
-// bracket are certainly in the support (only their count and sums of
-// (z-M), (z-M)^2 matter); the few inside it are listed and the support size
-// is resolved exactly: for a support of the K largest values, tau has a
-// closed form (sparsemax: (sum z - 1)/K; 1.5-entmax: the smaller root of
-// sum (z - tau)^2 = 1), and the right K is the one whose tau separates the
-// K-th and (K+1)-th values.  Sums are kept in 2^-40 fixed point so that the
-// result does not depend on the order the block visits the tokens.
-// General alpha, or a bracket holding too many tokens, falls back to
-// bisection in double over the candidates.
+// Bracket.  tau >= M - 1 with M = max z.  Moreover, if k page maxima are at
+// least c, those k tokens alone give sum (z - t)^r >= 1 at t = c - k^-(1/r),
+// so tau >= c - k^-(1/r); a 256-bin count of the page maxima near M gives
+// the best such c cheaply.  Only tokens above the resulting L can have
+// p > 0; they are staged in LDS.
+//
+// Exact solve (r in {1, 2}).  The staged values are counted into NB bins of
+// width w = 2^-m over [L, L + NB w] (w a power of two, so bin membership is
+// exact).  For the bin edge e_b, values in bin c >= b satisfy
+// (c-b) w <= z - e_b < (c+1-b) w, hence
+//   F_lo(b) = w^r sum_{c>=b} cnt_c (c-b)^r <= F(e_b) <= F_hi(b) = ... (c+1-b)^r
+// with F(t) = sum max(z - t, 0)^r; both are polynomials in b of suffix sums
+// of cnt_c c^k, exact in double.  The largest b with F_lo >= 1 and the
+// smallest with F_hi < 1 bracket tau.  Values above the bracket are in the
+// support (only their count, sum of (z - M) and of (z - M)^2 matter); the
+// few inside it are listed and the support size is resolved exactly: for a
+// support of the K largest values tau has a closed form (sparsemax:
+// (sum z - 1)/K; 1.5-entmax: the smaller root of sum (z - tau)^2 = 1), and
+// the right K is the one whose tau separates the K-th and (K+1)-th values.
+// Sums are kept in 2^-40 fixed point so that the result does not depend on
+// the order the block visits the tokens.  General alpha, or a bracket with
+// too many undecided tokens, falls back to bisection in double.
 // ---------------------------------------------------------------------------
-constexpr int kTauThreads = 256;
+constexpr int kTauThreads = 1024;
 constexpr int kTauBins = 2048;
 constexpr int kTauList = 1024;
-constexpr int kTauChunkCap = 4096;
+constexpr int kTauPageCap = 8192;
+constexpr int kTauCandCap = 16384;
+constexpr int kTauMaxBins = 1024;
 constexpr double kFix = 1099511627776.0;  // 2^40
 
 __device__ __forceinline__ long long fixp(double x) {
@@ -222,9 +370,9 @@ __device__ __forceinline__ long long block_sum_ll(long long x, long long *smem) 
   constexpr int NW = NT / kWave;
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
-  __syncthreads();
+  lds_barrier();
   long long r = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) r += smem[w];
@@ -236,9 +384,9 @@ __device__ __forceinline__ int block_max_i(int x, int *smem) {
   constexpr int NW = NT / kWave;
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, kWave));
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
-  __syncthreads();
+  lds_barrier();
   int r = smem[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = max(r, smem[w]);
@@ -247,6 +395,19 @@ __device__ __forceinline__ int block_max_i(int x, int *smem) {
 template <int NT>
 __device__ __forceinline__ int block_min_i(int x, int *smem) {
   return -block_max_i<NT>(-x, smem);
+}
+template <int NT>
+__device__ __forceinline__ double block_max_d(double x, double *smem) {
+  constexpr int NW = NT / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o, kWave));
+  lds_barrier();
+  if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
+  lds_barrier();
+  double r = smem[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmax(r, smem[w]);
+  return r;
 }
 
 // Inclusive scan of a double over the block (NT threads).
@@ -259,9 +420,9 @@ __device__ __forceinline__ double block_incl_scan_d(double x, double *smem) {
     const double y = __shfl_up(x, o, kWave);
     if (lane >= o) x += y;
   }
-  __syncthreads();
+  lds_barrier();
   if (lane == kWave - 1) smem[wid] = x;
-  __syncthreads();
+  lds_barrier();
   double base = 0.0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) base += (w < wid) ? smem[w] : 0.0;
@@ -269,97 +430,215 @@ __device__ __forceinline__ double block_incl_scan_d(double x, double *smem) {
 }
 
 __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
-    const float *__restrict__ zbuf, const float *__restrict__ cmax,
+    const float *__restrict__ zbuf, const float *__restrict__ pmax,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, int H, int G, int P, int cap, int maxch,
-    int r, float rg, float *__restrict__ tau_ws, float *__restrict__ tau_user) {
+    const int32_t *__restrict__ count, int H, int G, int P, int max_pages,
+    int cap, int r, float rg, float *__restrict__ tau_ws,
+    float *__restrict__ tau_user) {
+  constexpr int NW = kTauThreads / kWave;
+  constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
   __shared__ unsigned int hist[kTauBins];
-  __shared__ int chunks[kTauChunkCap];
+  __shared__ int cpages[NW][SEGP];
+  __shared__ float cand[kTauCandCap];
   __shared__ float list[kTauList];
-  __shared__ int s_nlist;
-  __shared__ float red_f[kTauThreads / kWave];
-  __shared__ int red_i[kTauThreads / kWave];
-  __shared__ double red_d[kTauThreads / kWave];
-  __shared__ long long red_ll[kTauThreads / kWave];
-  __shared__ int s_bestK;
+  __shared__ int s_ncand, s_nlist;
+  __shared__ int s_npg[NW];
+  __shared__ int s_seg[NW + 1];
+  __shared__ float red_f[NW];
+  __shared__ int red_i[NW];
+  __shared__ double red_d[NW];
+  __shared__ long long red_ll[NW];
   __shared__ double s_best_t;
   __shared__ double s_tot[3];
 
   const int ug = blockIdx.x, u = ug / G;
-  const int b = u / H;
-  const int tid = threadIdx.x;
-  const int len = seq_lens[b];
-  const int cnt = sel ? count[u] : n_pages_of(len, P);
-  const int ppc = kChunkTokens / P;
-  const int nch = (cnt + ppc - 1) / ppc;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   const float *zh = zbuf + static_cast<size_t>(ug) * cap;
-  const float *cm = cmax + static_cast<size_t>(ug) * maxch;
+  const float *pm = pmax + static_cast<size_t>(ug) * max_pages;
+  constexpr int U = 8;
 
-  // Largest score and the chunks that may hold candidates.
+  // Largest score.
   float mloc = -FLT_MAX;
-  for (int c = tid; c < nch; c += kTauThreads) mloc = fmaxf(mloc, cm[c]);
+  for (int j0 = tid; j0 < cnt; j0 += kTauThreads * U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int j = j0 + k * kTauThreads;
+      v[k] = j < cnt ? pm[j] : -FLT_MAX;
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) mloc = fmaxf(mloc, v[k]);
+  }
   const float M = block_max<kTauThreads>(mloc, red_f);
   const double Md = M;
-  const double Ld = Md - 1.0;
-  const int per = (nch + kTauThreads - 1) / kTauThreads;
-  const int c0 = tid * per, c1 = min(nch, c0 + per);
-  int ncand = 0;
-  for (int c = c0; c < c1; ++c) ncand += static_cast<double>(cm[c]) > Ld;
-  int n_chunks;
-  int cpos = block_excl_scan<kTauThreads>(ncand, red_i, n_chunks);
-  const bool chunk_list = n_chunks <= kTauChunkCap;
-  if (chunk_list)
-    for (int c = c0; c < c1; ++c)
-      if (static_cast<double>(cm[c]) > Ld) chunks[cpos++] = c;
-  for (int i = tid; i < kTauBins; i += kTauThreads) hist[i] = 0u;
-  if (tid == 0) s_nlist = 0;
-  __syncthreads();
-  const int n_iter_chunks = chunk_list ? n_chunks : nch;
-  const int ctoks = ppc * P;  // == kChunkTokens
-  // Visit every candidate token: fn(z) for z > L.
+
+  // Tighter lower bracket from the page maxima within 1 of M: with C_b the
+  // number of page maxima in bins >= b (all at least the bin's lower edge
+  // e_b), tau >= e_b - C_b^(-1/r).
+  static_assert(kTauMaxBins <= kTauBins, "page-maximum bins reuse hist");
+  for (int i = tid; i < kTauMaxBins; i += kTauThreads) hist[i] = 0u;
+  lds_barrier();
+  for (int j0 = tid; j0 < cnt; j0 += kTauThreads * U) {
+    float v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int j = j0 + k * kTauThreads;
+      v[k] = j < cnt ? pm[j] : -FLT_MAX;
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const double x = (static_cast<double>(v[k]) - (Md - 1.0)) * kTauMaxBins;
+      if (x > 0.0) {
+        const int bn = x < kTauMaxBins ? static_cast<int>(x) : kTauMaxBins - 1;
+        atomicAdd(&hist[bn], 1u);
+      }
+    }
+  }
+  lds_barrier();
+  double Lloc = Md - 1.0;
+  {
+    static_assert(kTauMaxBins == kTauThreads, "one bin per thread");
+    const int bin = kTauMaxBins - 1 - tid;  // thread 0 owns the top bin
+    int tot;
+    const int x = static_cast<int>(hist[bin]);
+    const int c = block_excl_scan<kTauThreads>(x, red_i, tot) + x;  // bins >= bin
+    if (c > 0) {
+      const double edge = (Md - 1.0) + static_cast<double>(bin) / kTauMaxBins;
+      const double kk = static_cast<double>(c);
+      const double drop = (r == 1) ? 1.0 / kk : (r == 2) ? 1.0 / sqrt(kk)
+                                   : pow(kk, -1.0 / static_cast<double>(rg));
+      Lloc = fmax(Lloc, edge - drop);
+    }
+  }
+  double L = block_max_d<kTauThreads>(Lloc, red_d);
+  // Snap down to a multiple of 2^-24 so that z - L is exact in double.
+  L = floor(L * 16777216.0) / 16777216.0;
+
+  // Pages whose maximum exceeds L: each wave lists, in page order, those of
+  // its interleaved 64-page tiles (no block barrier; loads batched).
+  int npw = 0;
+  for (int t0 = wave * kWave; t0 < cnt; t0 += kTauThreads * 2) {
+    float v[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = t0 + k * kTauThreads + lane;
+      v[k] = j < cnt ? pm[j] : -FLT_MAX;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = t0 + k * kTauThreads + lane;
+      const bool flag = j < cnt && static_cast<double>(v[k]) > L;
+      const unsigned long long ball = __ballot(flag);
+      const int rk = npw + __popcll(ball & ((1ull << lane) - 1ull));
+      if (flag && rk < SEGP) cpages[wave][rk] = j;
+      npw += __popcll(ball);
+    }
+  }
+  if (lane == 0) s_npg[wave] = npw;
+  if (tid == 0) { s_ncand = 0; s_nlist = 0; }
+  lds_barrier();
+  bool listed = true;
+  int n_listed = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    listed &= s_npg[w] <= SEGP;
+    n_listed += s_npg[w];
+  }
+  if (tid == 0) {
+    int acc = 0;
+    for (int w = 0; w < NW; ++w) { s_seg[w] = acc; acc += s_npg[w]; }
+    s_seg[NW] = acc;
+  }
+  lds_barrier();
+  const int n_pg = listed ? n_listed : cnt;
+  auto page_of = [&](int jj) {  // jj-th listed page (or jj itself)
+    if (!listed) return jj;
+    int w = 0;
+    for (int k = 1; k < NW; ++k) w += jj >= s_seg[k];
+    return cpages[w][jj - s_seg[w]];
+  };
+
+  // Stage the candidates z > L in LDS (order irrelevant downstream).
+  {
+    const int span = n_pg * P;
+    for (int base = 0; base < span; base += kTauThreads * U) {
+      float zv[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int fi = base + k * kTauThreads + tid;
+        zv[k] = -INFINITY;
+        if (fi < span) {
+          const int jj = fi / P, t = fi - jj * P;
+          const int j = page_of(jj);
+          if (listed || static_cast<double>(pm[j]) > L)
+            zv[k] = zh[static_cast<size_t>(j) * P + t];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (static_cast<double>(zv[k]) > L) {
+          const int sidx = atomicAdd(&s_ncand, 1);
+          if (sidx < kTauCandCap) cand[sidx] = zv[k];
+        }
+    }
+  }
+  lds_barrier();
+  const int ncand_all = s_ncand;
+  const bool staged = ncand_all <= kTauCandCap;
+  // Visit every candidate z > L: from LDS when staged, else from memory.
   auto for_candidates = [&](auto fn) {
-    for (int k = 0; k < n_iter_chunks; ++k) {
-      const int c = chunk_list ? chunks[k] : k;
-      if (!chunk_list && !(static_cast<double>(cm[c]) > Ld)) continue;
-      const int e = min(cnt * P, (c + 1) * ctoks);
-      for (int i = c * ctoks + tid; i < e; i += kTauThreads) {
-        const float z = zh[i];
-        if (static_cast<double>(z) > Ld) fn(z);
+    if (staged) {
+      for (int i = tid; i < ncand_all; i += kTauThreads) fn(cand[i]);
+    } else {
+      const int span = n_pg * P;
+      for (int fi = tid; fi < span; fi += kTauThreads) {
+        const int jj = fi / P, t = fi - jj * P;
+        const int j = page_of(jj);
+        if (!listed && !(static_cast<double>(pm[j]) > L)) continue;
+        const float z = zh[static_cast<size_t>(j) * P + t];
+        if (static_cast<double>(z) > L) fn(z);
       }
     }
   };
-  auto bin_of = [&](float z) {  // z > L on entry, so the bin is >= 0
-    const double x = floor((static_cast<double>(z) - Ld) * kTauBins);
+
+  // Bin width: the smallest power of two w with NB * w >= M - L.
+  double w = 1.0;
+  for (int it = 0; it < 64 && w * kTauBins < Md - L; ++it) w *= 2.0;
+  for (int it = 0; it < 64 && w * 0.5 * kTauBins >= Md - L; ++it) w *= 0.5;
+  const double inv_w = 1.0 / w;
+  auto bin_of = [&](float z) {  // z > L on entry
+    const double x = floor((static_cast<double>(z) - L) * inv_w);
     return x < kTauBins ? (x > 0.0 ? static_cast<int>(x) : 0) : kTauBins - 1;
   };
 
   double t_rel = 0.0;  // tau - M
   bool solved = false;
-  double blo = Ld, bhi = Md;  // bisection bracket for the fallback
+  double blo = L, bhi = Md;  // bracket for the fallback
   if (r == 1 || r == 2) {
+    for (int i = tid; i < kTauBins; i += kTauThreads) hist[i] = 0u;
+    lds_barrier();
     for_candidates([&](float z) { atomicAdd(&hist[bin_of(z)], 1u); });
-    __syncthreads();
-    // Suffix sums of cnt, cnt*c, cnt*c^2; thread t owns bins [8t, 8t+8).
+    lds_barrier();
     constexpr int BPT = kTauBins / kTauThreads;
     double l0 = 0, l1 = 0, l2 = 0;
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
-      const double cb = tid * BPT + k, n = hist[tid * BPT + k];
-      l0 += n; l1 += n * cb; l2 += n * cb * cb;
+      const double cb = tid * BPT + k, nn = hist[tid * BPT + k];
+      l0 += nn; l1 += nn * cb; l2 += nn * cb * cb;
     }
     const double i0 = block_incl_scan_d<kTauThreads>(l0, red_d);
     const double i1 = block_incl_scan_d<kTauThreads>(l1, red_d);
     const double i2 = block_incl_scan_d<kTauThreads>(l2, red_d);
-    // Totals (the last thread's inclusive values) via LDS broadcast.
     if (tid == kTauThreads - 1) { s_tot[0] = i0; s_tot[1] = i1; s_tot[2] = i2; }
-    __syncthreads();
-    // Suffix sums strictly after this thread's bins.
+    lds_barrier();
     double S0 = s_tot[0] - i0, S1 = s_tot[1] - i1, S2 = s_tot[2] - i2;
-    const double NB = kTauBins, need = (r == 2) ? NB * NB : NB;
-    int my_lo = 0, my_hi = kTauBins;  // b = NB always has F_hi = 0 < 1
+    // F_lo(b) >= 1  <=>  sum cnt (c-b)^r >= w^-r
+    const double need = (r == 2) ? inv_w * inv_w : inv_w;
+    int my_lo = 0, my_hi = kTauBins;  // F_hi at the top edge is <= 0 < 1
     for (int k = BPT - 1; k >= 0; --k) {
-      const double bb = tid * BPT + k, n = hist[tid * BPT + k];
-      S0 += n; S1 += n * bb; S2 += n * bb * bb;
+      const double bb = tid * BPT + k, nn = hist[tid * BPT + k];
+      S0 += nn; S1 += nn * bb; S2 += nn * bb * bb;
       double flo, fhi;
       if (r == 2) {
         flo = S2 - 2.0 * bb * S1 + bb * bb * S0;
@@ -373,18 +652,15 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     }
     const int b_lo = block_max_i<kTauThreads>(my_lo, red_i);
     const int b_hi = block_min_i<kTauThreads>(my_hi, red_i);
-    blo = Ld + static_cast<double>(b_lo) / kTauBins;
-    bhi = Ld + static_cast<double>(b_hi) / kTauBins;
+    blo = L + b_lo * w;
+    bhi = fmin(Md, L + b_hi * w);
 
-    // Certain support (bin >= b_hi) and the undecided tokens.
     long long nfix = 0, sy = 0, sy2 = 0;
-    int minbin_fix = kTauBins;
     for_candidates([&](float z) {
       const int bn = bin_of(z);
       if (bn >= b_hi) {
         const double y = static_cast<double>(z) - Md;
         ++nfix; sy += fixp(y); sy2 += fixp(y * y);
-        minbin_fix = min(minbin_fix, bn);
       } else if (bn >= b_lo) {
         const int slot = atomicAdd(&s_nlist, 1);
         if (slot < kTauList) list[slot] = z;
@@ -393,23 +669,16 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     nfix = block_sum_ll<kTauThreads>(nfix, red_ll);
     sy = block_sum_ll<kTauThreads>(sy, red_ll);
     sy2 = block_sum_ll<kTauThreads>(sy2, red_ll);
-    // (block_sum_ll ends with a barrier, so s_nlist is final here.)
-    const int nl = s_nlist;
-    // Smallest certain value: the least z over bins >= b_hi is needed only
-    // through "tau <= every certain value", which holds whenever tau < e_bhi.
+    const int nl = s_nlist;  // final: block_sum_ll ends with a barrier
     if (nl <= kTauList) {
-      if (tid == 0) { s_bestK = -1; s_best_t = 0.0; }
-      __syncthreads();
-      const double ylo_floor = blo - Md;  // every untracked value is below
-      const double ybound_hi = bhi - Md;  // every certain value is >= this
-      // Candidate supports: the certain set plus the list values >= z_j
-      // (ties ordered by list index), and the certain set alone (j = nl).
+      const double ylo_floor = blo - Md;             // untracked values are below
+      const double ybound_hi = (L + b_hi * w) - Md;  // certain values are >= this
       int bestK = -1;
       double best_t = 0.0;
       for (int j = tid; j <= nl; j += kTauThreads) {
         const float zj = j < nl ? list[j] : 0.f;
         long long K = nfix, SY = sy, SY2 = sy2;
-        double ynext = ylo_floor;  // largest value left out
+        double ynext = ylo_floor;
         for (int i = 0; i < nl; ++i) {
           const float zi = list[i];
           const bool in = j < nl && (zi > zj || (zi == zj && i <= j));
@@ -438,27 +707,28 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         }
       }
       const int K_all = block_max_i<kTauThreads>(bestK, red_i);
-      if (K_all >= 0 && bestK == K_all) s_best_t = best_t;  // unique K
-      __syncthreads();
+      if (K_all >= 0 && bestK == K_all) s_best_t = best_t;
+      lds_barrier();
       if (K_all >= 0) {
         t_rel = s_best_t;
         solved = true;
       }
     }
-    (void)minbin_fix;
   }
   if (!solved) {
-    // Bisection in double on [blo, bhi] over all candidates.
+    // Bisection in double on [blo, bhi] over the candidates.
     double lo = blo, hi = bhi;
     for (int it = 0; it < 64 && hi - lo > 1e-12 * fmax(1.0, fabs(hi)); ++it) {
       const double mid = 0.5 * (lo + hi);
-      double f = 0.0;
+      double fsum = 0.0;
       for_candidates([&](float z) {
         const double d = static_cast<double>(z) - mid;
-        if (d > 0.0) f += (r == 1) ? d : (r == 2) ? d * d : pow(d, static_cast<double>(rg));
+        if (d > 0.0)
+          fsum += (r == 1) ? d : (r == 2) ? d * d
+                                          : pow(d, static_cast<double>(rg));
       });
-      f = block_sum_d<kTauThreads>(f, red_d);
-      if (f >= 1.0) lo = mid; else hi = mid;
+      fsum = block_sum_d<kTauThreads>(fsum, red_d);
+      if (fsum >= 1.0) lo = mid; else hi = mid;
     }
     t_rel = 0.5 * (lo + hi) - Md;
   }
@@ -470,183 +740,259 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
 }
 
 // ---------------------------------------------------------------------------
-// 3a. Apply: chunk partials of sum_i p_i v_i and sum_i p_i.
+// Chunks: kChunkTokens token positions (kChunkTokens / P pages) of one unit.
 // ---------------------------------------------------------------------------
+struct ChunkPages {
+  int lp[kMaxChunkPages];
+  int slot[kMaxChunkPages];
+  int nt[kMaxChunkPages];
+};
+
+// Stages the pages of chunk c of unit u; returns the number of pages.
+__device__ __forceinline__ int stage_chunk(ChunkPages &cp,
+                                           const int32_t *page_table,
+                                           const int32_t *seq_lens,
+                                           const int32_t *sel, int u, int c,
+                                           int cnt, int H, int P,
+                                           int max_pages) {
+  const int b = u / H;
+  const int ppc = kChunkTokens / P;
+  const int j0 = c * ppc;
+  const int npg = min(cnt - j0, ppc);
+  if (threadIdx.x < npg) {
+    const int j = j0 + threadIdx.x;
+    const int lp = sel ? sel[static_cast<size_t>(u) * max_pages + j] : j;
+    cp.lp[threadIdx.x] = lp;
+    cp.slot[threadIdx.x] = page_table[static_cast<size_t>(b) * max_pages + lp];
+    cp.nt[threadIdx.x] = page_tokens(lp, seq_lens[b], P);
+  }
+  return npg;
+}
+
+// ---------------------------------------------------------------------------
+// 3a. Apply: chunk partials of sum_i p_i v_i and sum_i p_i.  Persistent
+// blocks over chunks.  A chunk none of whose pages has a maximum above tau
+// for any head is skipped.  Otherwise p is computed once per (token, head)
+// into LDS from the z of the chunk's active pages, the rows with some p > 0
+// are compacted, and all their value loads are issued together.
+// ---------------------------------------------------------------------------
+constexpr int kRowUnroll = 4;
+
 template <class E, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
     const typename E::T *__restrict__ vpool,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, int H, int P, int max_pages, int cap,
-    int maxch, int r, float rg, const float *__restrict__ zbuf,
-    const float *__restrict__ cmax, const float *__restrict__ tau,
+    const int32_t *__restrict__ count, int units, int H, int P, int max_pages,
+    int cap, int maxch, int r, float rg, const float *__restrict__ zbuf,
+    const float *__restrict__ pmax, const float *__restrict__ tau,
     float *__restrict__ part_o, float *__restrict__ part_s,
     float *__restrict__ probs) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
-  constexpr int STEP = kDecWaves * TPW * kUnroll;
+  constexpr int ROWS_STEP = kDecWaves * TPW * kRowUnroll;
+  __shared__ int pref[kMaxUnits + 1];
+  __shared__ int tmp[kDecWaves];
   __shared__ ChunkPages cp;
+  __shared__ int s_act[kMaxChunkPages];
+  __shared__ float s_p[G][kChunkTokens];
+  __shared__ int s_rows[kChunkTokens];
   __shared__ float s_acc[kDecWaves][G][D];
   __shared__ float s_sp[kDecWaves][G];
-  const int u = blockIdx.y, c = blockIdx.x;
-  const int h = u % H, b = u / H;
-  int j0, j1, len;
-  if (!stage_chunk(cp, page_table, seq_lens, sel, count, u, H, P, max_pages,
-                   c, j0, j1, len))
-    return;
-  float tg[G];
-  bool active = false;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    tg[g] = tau[u * G + g];
-    active |= cmax[(static_cast<size_t>(u) * G + g) * maxch + c] > tg[g];
-  }
-  if (!active) return;  // no token of this chunk has p > 0
+  const int ppc = kChunkTokens / P;
+  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
+                                                   count, units, H, P, ppc);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
   const int Hq = H * G;
   const size_t pstride = static_cast<size_t>(max_pages) * P;
-  const int npos = (j1 - j0) * P;
-  const float *zu = zbuf + static_cast<size_t>(u) * G * cap;
 
-  float acc[G][8], sp[G];
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int u = find_unit(pref, units, w);
+    const int c = w - pref[u];
+    const int h = u % H, b = u / H;
+    const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+    const int j0 = c * ppc;
+    const int npg = min(cnt - j0, ppc);
+    // Active pages: some head's page maximum above its tau.
+    bool act = false;
+    if (threadIdx.x < npg) {
+      const int jj = threadIdx.x;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    sp[g] = 0.f;
+      for (int g = 0; g < G; ++g)
+        act |= pmax[(static_cast<size_t>(u) * G + g) * max_pages + j0 + jj] >
+               tau[u * G + g];
+      s_act[jj] = act;
+    }
+    if (!__syncthreads_or(act)) continue;
+    stage_chunk(cp, page_table, seq_lens, sel, u, c, cnt, H, P, max_pages);
+    float tg[G];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
-  }
-  for (int base = 0; base < kChunkTokens; base += STEP) {
-    float p[kUnroll][G];
-    float x[kUnroll][8];
-    bool any[kUnroll];
+    for (int g = 0; g < G; ++g) tg[g] = tau[u * G + g];
+    lds_barrier();
+    const int npos = npg * P;
+    const float *zu = zbuf + static_cast<size_t>(u) * G * cap +
+                      static_cast<size_t>(j0) * P;
+    // p for every position of the chunk (zero outside active pages).
+    float spl[G];
 #pragma unroll
-    for (int rr = 0; rr < kUnroll; ++rr) {
-      const int i = base + (rr * kDecWaves + wave) * TPW + sub;
+    for (int g = 0; g < G; ++g) spl[g] = 0.f;
+    int n_rows = 0;
+    for (int base = 0; base < kChunkTokens; base += kDecThreads) {
+      const int i = base + threadIdx.x;
       const int jj = i / P, t = i - jj * P;
-      const bool valid = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-      any[rr] = false;
+      const bool on = i < npos && s_act[jj] && t < cp.nt[jj];
+      float pv[G];
+      bool any = false;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float pv = 0.f;
-        if (valid) {
-          const float z = zu[static_cast<size_t>(g) * cap + static_cast<size_t>(j0) * P + i];
-          pv = pow_r(fmaxf(z - tg[g], 0.f), r, rg);
-        }
-        p[rr][g] = pv;
-        any[rr] |= pv > 0.f;
+        pv[g] = 0.f;
+        if (on) pv[g] = pow_r(fmaxf(zu[static_cast<size_t>(g) * cap + i] - tg[g], 0.f), r, rg);
+        s_p[g][i] = pv[g];
+        spl[g] += pv[g];
+        any |= pv[g] > 0.f;
       }
-      if (any[rr]) {
-        load8(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x[rr]);
-      }
-      if (probs && valid) {
+      if (probs && on) {
         const size_t tok = static_cast<size_t>(cp.lp[jj]) * P + t;
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          if (li == g)
-            probs[(static_cast<size_t>(b) * Hq + h * G + g) * pstride + tok] = p[rr][g];
+          probs[(static_cast<size_t>(b) * Hq + h * G + g) * pstride + tok] = pv[g];
       }
+      int tot;
+      const int rk = tile_rank<kDecThreads>(any, tmp, tot);
+      if (any) s_rows[n_rows + rk] = i;
+      n_rows += tot;
     }
 #pragma unroll
-    for (int rr = 0; rr < kUnroll; ++rr) {
-      if (any[rr]) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(p[rr][g], x[rr][j], acc[g][j]);
-          if (li == 0) sp[g] += p[rr][g];
-        }
-      }
+    for (int g = 0; g < G; ++g) {
+      const float sg = group_sum<kWave>(spl[g]);
+      if (lane == 0) s_sp[wave][g] = sg;
     }
-  }
-  // Merge the TPW token groups of the wave (lanes with equal li), then waves.
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = acc[g][j];
-#pragma unroll
-      for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-      acc[g][j] = v;
-    }
-    const float s = group_sum<kWave>(sp[g]);
-    if (lane == 0) s_sp[wave][g] = s;
-  }
-  if (sub == 0) {
+    lds_barrier();
+    // Value rows with some p > 0: LPT lanes per row, all loads in flight.
+    float acc[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
-  }
-  __syncthreads();
-  float *po = part_o + (static_cast<size_t>(u) * maxch + c) * G * D;
-  for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
-    const int g = e / D, d = e % D;
-    float v = s_acc[0][g][d];
+      for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
+    for (int base = 0; base < n_rows; base += ROWS_STEP) {
+      float x[kRowUnroll][8];
+      int ri[kRowUnroll];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) v += s_acc[w][g][d];
-    po[e] = v;
-  }
-  if (threadIdx.x < G) {
-    float v = s_sp[0][threadIdx.x];
+      for (int rr = 0; rr < kRowUnroll; ++rr) {
+        const int k = base + (rr * kDecWaves + wave) * TPW + sub;
+        ri[rr] = k < n_rows ? s_rows[k] : -1;
+        if (ri[rr] >= 0) {
+          const int jj = ri[rr] / P, t = ri[rr] - jj * P;
+          load8(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x[rr]);
+        }
+      }
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) v += s_sp[w][threadIdx.x];
-    part_s[(static_cast<size_t>(u) * maxch + c) * G + threadIdx.x] = v;
+      for (int rr = 0; rr < kRowUnroll; ++rr)
+        if (ri[rr] >= 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pw = s_p[g][ri[rr]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(pw, x[rr][j], acc[g][j]);
+          }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = acc[g][j];
+#pragma unroll
+        for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+        acc[g][j] = v;
+      }
+    if (sub == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
+    }
+    lds_barrier();
+    float *po = part_o + (static_cast<size_t>(u) * maxch + c) * G * D;
+    for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
+      const int g = e / D, d = e % D;
+      float v = s_acc[0][g][d];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww) v += s_acc[ww][g][d];
+      po[e] = v;
+    }
+    if (threadIdx.x < G) {
+      float v = s_sp[0][threadIdx.x];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww) v += s_sp[ww][threadIdx.x];
+      part_s[(static_cast<size_t>(u) * maxch + c) * G + threadIdx.x] = v;
+    }
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
 // 3b. Merge chunk partials in chunk order: out = sum_c o_c / sum_c s_c over
-// the chunks whose maximum exceeds tau (the others contribute exact zeros).
-// One block per query head; D threads per chunk slice.
+// the chunks holding a page whose maximum exceeds tau for this head (every
+// other chunk contributes exact zeros).  One block per query head.
 // ---------------------------------------------------------------------------
 constexpr int kCombThreads = 1024;
+constexpr int kCombActCap = 4096;
 
 __global__ __launch_bounds__(kCombThreads) void k_entmax_combine(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, int H, int G, int D, int P, int maxch,
-    const float *__restrict__ cmax, const float *__restrict__ tau,
-    const float *__restrict__ part_o, const float *__restrict__ part_s,
-    float *__restrict__ out) {
-  __shared__ int act[kTauChunkCap];
+    const int32_t *__restrict__ count, int H, int G, int D, int P,
+    int max_pages, int maxch, const float *__restrict__ pmax,
+    const float *__restrict__ tau, const float *__restrict__ part_o,
+    const float *__restrict__ part_s, float *__restrict__ out) {
+  __shared__ int act[kCombActCap];
   __shared__ int red_i[kCombThreads / kWave];
   __shared__ float s_o[kCombThreads];
   __shared__ float s_s[kCombThreads];
-  const int ug = blockIdx.x, u = ug / G, g = ug % G, b = u / H;
+  const int ug = blockIdx.x, u = ug / G, g = ug % G;
   const int tid = threadIdx.x;
-  const int len = seq_lens[b];
-  const int cnt = sel ? count[u] : n_pages_of(len, P);
+  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   const int ppc = kChunkTokens / P;
   const int nch = (cnt + ppc - 1) / ppc;
   const float t = tau[ug];
-  const float *cm = cmax + static_cast<size_t>(ug) * maxch;
-  const int per = (nch + kCombThreads - 1) / kCombThreads;
-  const int c0 = tid * per, c1 = min(nch, c0 + per);
-  int na = 0;
-  for (int c = c0; c < c1; ++c) na += cm[c] > t;
-  int nact;
-  int pos = block_excl_scan<kCombThreads>(na, red_i, nact);
-  const bool listed = nact <= kTauChunkCap;
-  if (listed)
-    for (int c = c0; c < c1; ++c)
-      if (cm[c] > t) act[pos++] = c;
-  __syncthreads();
+  const float *pm = pmax + static_cast<size_t>(ug) * max_pages;
+  int nact = 0;
+  for (int base = 0; base < nch; base += kCombThreads) {
+    const int c = base + tid;
+    bool flag = false;
+    if (c < nch) {
+      const int j1 = min(cnt, (c + 1) * ppc);
+      for (int j = c * ppc; j < j1; ++j) flag |= pm[j] > t;
+    }
+    int tot;
+    const int rk = tile_rank<kCombThreads>(flag, red_i, tot);
+    if (flag && nact + rk < kCombActCap) act[nact + rk] = c;
+    nact += tot;
+  }
+  lds_barrier();
+  const bool listed = nact <= kCombActCap;
   const int slices = kCombThreads / D;
   const int d = tid % D, sl = tid / D;
   float o = 0.f, s = 0.f;
-  if (sl < slices) {
-    const int n = listed ? nact : nch;
-    for (int k = sl; k < n; k += slices) {
-      const int c = listed ? act[k] : k;
-      if (!listed && !(cm[c] > t)) continue;
-      const size_t base = static_cast<size_t>(u) * maxch + c;
-      o += part_o[(base * G + g) * D + d];
-      if (d == 0) s += part_s[base * G + g];
+  const int n = listed ? nact : nch;
+  for (int k = sl; k < n; k += slices) {
+    int c = k;
+    if (listed) {
+      c = act[k];
+    } else {
+      const int j1 = min(cnt, (c + 1) * ppc);
+      bool any = false;
+      for (int j = c * ppc; j < j1; ++j) any |= pm[j] > t;
+      if (!any) continue;
     }
+    const size_t base = static_cast<size_t>(u) * maxch + c;
+    o += part_o[(base * G + g) * D + d];
+    if (d == 0) s += part_s[base * G + g];
   }
   s_o[tid] = o;
   s_s[tid] = s;
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     float oo = 0.f, ss = 0.f;
     for (int k = 0; k < slices; ++k) {
@@ -668,9 +1014,129 @@ __global__ void k_fill_probs(const int32_t *__restrict__ seq_lens, int Hq,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K softmax: per chunk, scores to LDS, chunk max m, l = sum exp(s - m),
-// acc = sum exp(s - m) v; then a log-sum-exp merge over chunks.
+// Split-K softmax.  Persistent blocks over chunks: scores into LDS (matrix
+// cores for bfloat16 keys), the chunk maximum m, the weights exp(s - m)
+// once per (token, head), then the weighted value sum on the vector units.
+// The chunk partials (m, l, acc) are merged in log-sum-exp form.
 // ---------------------------------------------------------------------------
+template <class E, int D, int G>
+__device__ __forceinline__ void chunk_scores_valu(
+    const ChunkPages &cp, const typename E::T *kpool, const float *q, int b,
+    int h, int H, int P, int npos, float scale, float (*s_sc)[kChunkTokens]) {
+  constexpr int LPT = D / 8;
+  constexpr int TPW = kWave / LPT;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
+  const int Hq = H * G;
+  float qs[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qs[g][j] = q[(static_cast<size_t>(b) * Hq + h * G + g) * D + d0 + j] * scale;
+  for (int i0 = wave * TPW; i0 < kChunkTokens; i0 += kDecWaves * TPW) {
+    const int i = i0 + sub;
+    const int jj = i / P, t = i - jj * P;
+    const bool valid = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
+    float x[8];
+    if (valid) {
+      load8(kpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[j], a);
+      a = group_sum<LPT>(a);
+      if (li == g) s_sc[g][i] = valid ? a : -INFINITY;
+    }
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void chunk_scores_mfma(
+    const ChunkPages &cp, const uint16_t *kpool, const float *q, int b, int h,
+    int H, int P, int npos, float scale, float (*s_sc)[kChunkTokens]) {
+  constexpr int KS = D / 32;
+  constexpr int NPASS = (G + 3) / 4;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15, kb = lane >> 4;
+  bf16x8_t a[NPASS][KS];
+  load_q_parts<D, G>(a, q, b, h, H, scale);
+  // Each wave takes 16-token groups wave, wave+4, ...; 4 groups in flight.
+  constexpr int NGR = kChunkTokens / 16;
+  constexpr int INF = 4;
+  for (int gr0 = wave; gr0 < NGR; gr0 += INF * kDecWaves) {
+    bf16x8_t bv[INF][KS];
+#pragma unroll
+    for (int k = 0; k < INF; ++k) {
+      const int i = 16 * (gr0 + k * kDecWaves) + n;
+      const int jj = i / P, t = i - jj * P;
+      const bool inb = i < npos;
+      const int slot = cp.slot[inb ? jj : 0];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (inb)
+          bv[k][s] = *reinterpret_cast<const bf16x8_t *>(
+              kpool + pool_row(slot, h, t, H, P, D) + 32 * s + 8 * kb);
+        else
+          bv[k][s] = bf16x8_t{};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < INF; ++k) {
+      const int i = 16 * (gr0 + k * kDecWaves) + n;
+      const int jj = i / P, t = i - jj * P;
+      const bool valid = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
+#pragma unroll
+      for (int ps = 0; ps < NPASS; ++ps) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], bv[k][s], c, 0, 0, 0);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float p1 = __shfl_down(c[ii], 16, kWave);
+          const float p2 = __shfl_down(c[ii], 32, kWave);
+          const int g = 4 * ps + ii;
+          if (g < G && lane < 16) s_sc[g][i] = valid ? c[ii] + (p1 + p2) : -INFINITY;
+        }
+      }
+    }
+  }
+}
+
+// Eight consecutive elements kept packed until use (fewer registers while
+// many rows are in flight).
+template <class E>
+struct Packed8;
+template <>
+struct Packed8<BF16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t *p) {
+    w = *reinterpret_cast<const uint4 *>(p);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+};
+template <>
+struct Packed8<F32> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float *p) {
+    a = *reinterpret_cast<const float4 *>(p);
+    b = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+
 template <class E, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void k_softmax_partial(
     const typename E::T *__restrict__ kpool,
@@ -678,192 +1144,365 @@ __global__ __launch_bounds__(kDecThreads) void k_softmax_partial(
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
-    float scale, int H, int P, int max_pages, int maxch,
+    float scale, int units, int H, int P, int max_pages, int maxch,
     float *__restrict__ part_m, float *__restrict__ part_l,
     float *__restrict__ part_o) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
-  constexpr int STEP = kDecWaves * TPW * kUnroll;
+  constexpr int VSTEP = 256;                      // value rows per sub-tile
+  constexpr int VUN = VSTEP / (kDecWaves * TPW);  // rows per lane in flight
+  __shared__ int pref[kMaxUnits + 1];
+  __shared__ int tmp[kDecWaves];
   __shared__ ChunkPages cp;
   __shared__ float s_sc[G][kChunkTokens];
   __shared__ float s_acc[kDecWaves][G][D];
   __shared__ float red[kDecWaves][G];
-  const int u = blockIdx.y, c = blockIdx.x;
-  const int h = u % H, b = u / H;
-  int j0, j1, len;
-  if (!stage_chunk(cp, page_table, seq_lens, sel, count, u, H, P, max_pages,
-                   c, j0, j1, len))
-    return;
+  const int ppc = kChunkTokens / P;
+  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
+                                                   count, units, H, P, ppc);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
-  const int Hq = H * G;
-  const int npos = (j1 - j0) * P;
-  float qs[G][8];
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int u = find_unit(pref, units, w);
+    const int c = w - pref[u];
+    const int h = u % H, b = u / H;
+    const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+    const int npg = stage_chunk(cp, page_table, seq_lens, sel, u, c, cnt, H, P,
+                                max_pages);
+    lds_barrier();
+    const int npos = npg * P;
+    if constexpr (sizeof(typename E::T) == 2)
+      chunk_scores_mfma<D, G>(cp, reinterpret_cast<const uint16_t *>(kpool), q,
+                              b, h, H, P, npos, scale, s_sc);
+    else
+      chunk_scores_valu<E, D, G>(cp, kpool, q, b, h, H, P, npos, scale, s_sc);
+    lds_barrier();
+    // chunk maximum per head, then the weights and their sum
+    float m[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float *qg = q + (static_cast<size_t>(b) * Hq + h * G + g) * D + d0;
+    for (int g = 0; g < G; ++g) {
+      float x = -FLT_MAX;
+      for (int i = threadIdx.x; i < kChunkTokens; i += kDecThreads)
+        x = fmaxf(x, s_sc[g][i]);
+      x = group_max<kWave>(x);
+      if (lane == 0) red[wave][g] = x;
+    }
+    lds_barrier();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qs[g][j] = qg[j] * scale;
-  }
-  float mx[G];
+    for (int g = 0; g < G; ++g) {
+      m[g] = red[0][g];
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -FLT_MAX;
-  for (int base = 0; base < kChunkTokens; base += STEP) {
-    float x[kUnroll][8];
-    bool valid[kUnroll];
-    int pos[kUnroll];
+      for (int ww = 1; ww < kDecWaves; ++ww) m[g] = fmaxf(m[g], red[ww][g]);
+    }
+    lds_barrier();
 #pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-      const int i = base + (r * kDecWaves + wave) * TPW + sub;
-      const int jj = i / P, t = i - jj * P;
-      pos[r] = i;
-      valid[r] = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-      if (valid[r]) load8(kpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x[r]);
-      else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[r][j] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      float x = 0.f;
+      for (int i = threadIdx.x; i < kChunkTokens; i += kDecThreads) {
+        const float pw = expf(s_sc[g][i] - m[g]);  // exp(-inf) = 0
+        s_sc[g][i] = pw;
+        x += pw;
       }
+      x = group_sum<kWave>(x);
+      if (lane == 0) red[wave][g] = x;
     }
-#pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[r][j], a);
-        a = group_sum<LPT>(a);
-        if (li == g) s_sc[g][pos[r]] = valid[r] ? a : -INFINITY;
-        if (valid[r]) mx[g] = fmaxf(mx[g], a);
-      }
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = group_max<kWave>(mx[g]);
-    if (lane == 0) red[wave][g] = m;
-  }
-  __syncthreads();
-  float m[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = red[0][g];
-#pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) m[g] = fmaxf(m[g], red[w][g]);
-  }
-  float acc[G][8], l[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l[g] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
-  }
-  for (int base = 0; base < kChunkTokens; base += STEP) {
-    float x[kUnroll][8];
-    bool valid[kUnroll];
-    int pos[kUnroll];
-#pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-      const int i = base + (r * kDecWaves + wave) * TPW + sub;
-      const int jj = i / P, t = i - jj * P;
-      pos[r] = i;
-      valid[r] = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-      if (valid[r]) load8(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0, x[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < kUnroll; ++r) {
-      if (valid[r]) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pw = expf(s_sc[g][pos[r]] - m[g]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(pw, x[r][j], acc[g][j]);
-          if (li == 0) l[g] += pw;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float v = acc[g][j];
-#pragma unroll
-      for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-      acc[g][j] = v;
-    }
-    l[g] = group_sum<kWave>(l[g]);
-  }
-  __syncthreads();  // red[] reused below
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) red[wave][g] = l[g];
-  }
-  if (sub == 0) {
+    lds_barrier();
+    float acc[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
-  }
-  __syncthreads();
-  const size_t pc = static_cast<size_t>(u) * maxch + c;
-  float *po = part_o + pc * G * D;
-  for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
-    const int g = e / D, d = e % D;
-    float v = s_acc[0][g][d];
+      for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
+    for (int base = 0; base < npos; base += VSTEP) {
+      Packed8<E> x[VUN];
+      bool valid[VUN];
+      int pos[VUN];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) v += s_acc[w][g][d];
-    po[e] = v;
-  }
-  if (threadIdx.x < G) {
-    float v = red[0][threadIdx.x];
+      for (int rr = 0; rr < VUN; ++rr) {
+        const int i = base + (rr * kDecWaves + wave) * TPW + sub;
+        const int jj = i / P, t = i - jj * P;
+        pos[rr] = i;
+        valid[rr] = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
+        if (valid[rr]) x[rr].load(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0);
+      }
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) v += red[w][threadIdx.x];
-    part_l[pc * G + threadIdx.x] = v;
-    part_m[pc * G + threadIdx.x] = m[threadIdx.x];
+      for (int rr = 0; rr < VUN; ++rr) {
+        if (valid[rr]) {
+          float xv[8];
+          x[rr].unpack(xv);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pw = s_sc[g][pos[rr]];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(pw, xv[j], acc[g][j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = acc[g][j];
+#pragma unroll
+        for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+        acc[g][j] = v;
+      }
+    if (sub == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
+    }
+    lds_barrier();
+    const size_t pc = static_cast<size_t>(u) * maxch + c;
+    float *po = part_o + pc * G * D;
+    for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
+      const int g = e / D, d = e % D;
+      float v = s_acc[0][g][d];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww) v += s_acc[ww][g][d];
+      po[e] = v;
+    }
+    if (threadIdx.x < G) {
+      float v = red[0][threadIdx.x];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww) v += red[ww][threadIdx.x];
+      part_l[pc * G + threadIdx.x] = v;
+      part_m[pc * G + threadIdx.x] = m[threadIdx.x];
+    }
+    lds_barrier();
   }
 }
 
-__global__ __launch_bounds__(kCombThreads) void k_softmax_combine(
+// Split-K softmax on the matrix cores (bfloat16 K/V).  Within a chunk every
+// wave runs its own online softmax over 16-token groups: scores of a group
+// from one MFMA pass, the group maximum m', the running state rescaled by
+// exp(m - m'), weights exp(s - m') broadcast to the lanes that hold the
+// group's value rows.  The K and V rows of two groups are in flight at once
+// and waves never wait for each other until the chunk's four states are
+// merged.
+template <int D, int G>
+__global__ __launch_bounds__(kDecThreads) void k_softmax_partial_mfma(
+    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
+    const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
+    const int32_t *__restrict__ count, const float *__restrict__ q,
+    float scale, int units, int H, int P, int max_pages, int maxch,
+    float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_o) {
+  constexpr int KS = D / 32;
+  constexpr int NPASS = (G + 3) / 4;
+  constexpr int LPT = D / 8;      // lanes per value row
+  constexpr int TPI = kWave / LPT;  // value rows per load instruction
+  constexpr int NVI = 16 / TPI;   // value load instructions per 16 tokens
+  constexpr int NGR = kChunkTokens / 16;
+  __shared__ int pref[kMaxUnits + 1];
+  __shared__ int tmp[kDecWaves];
+  __shared__ ChunkPages cp;
+  __shared__ float s_m[kDecWaves][G];
+  __shared__ float s_l[kDecWaves][G];
+  __shared__ float s_acc[kDecWaves][G][D];
+  const int ppc = kChunkTokens / P;
+  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
+                                                   count, units, H, P, ppc);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15;
+  const int li = lane % LPT, sub = lane / LPT, d0 = li * 8;
+  bf16x8_t a[NPASS][KS];
+  int cur_u = -1;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int u = find_unit(pref, units, w);
+    const int c = w - pref[u];
+    const int h = u % H, b = u / H;
+    const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+    const int npg = stage_chunk(cp, page_table, seq_lens, sel, u, c, cnt, H, P,
+                                max_pages);
+    lds_barrier();
+    if (u != cur_u) {
+      cur_u = u;
+      load_q_parts<D, G>(a, q, b, h, H, scale);
+    }
+    const int npos = npg * P;
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
+    }
+    for (int gr0 = wave; gr0 < NGR; gr0 += 2 * kDecWaves) {
+      bf16x8_t kbv[2][KS];
+      Packed8<BF16> vv[2][NVI];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int base = 16 * (gr0 + e * kDecWaves);
+        {
+          const int i = base + n;
+          const int jj = i / P, t = i - jj * P;
+          const bool inb = i < npos;
+          const int slot = cp.slot[inb ? jj : 0];
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            kbv[e][s] = inb ? *reinterpret_cast<const bf16x8_t *>(
+                                  kpool + pool_row(slot, h, t, H, P, D) + 32 * s + 8 * kb_of(lane))
+                            : bf16x8_t{};
+        }
+#pragma unroll
+        for (int vi = 0; vi < NVI; ++vi) {
+          const int i = base + vi * TPI + sub;
+          const int jj = i / P, t = i - jj * P;
+          if (i < npos)
+            vv[e][vi].load(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int base = 16 * (gr0 + e * kDecWaves);
+        const int i = base + n;
+        const int jj = i / P, t = i - jj * P;
+        const bool valid = lane < 16 && i < npos &&
+                           t < cp.nt[jj < kMaxChunkPages ? jj : 0];
+        float sv[G];
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+          f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], kbv[e][s], cc, 0, 0, 0);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float p1 = __shfl_down(cc[ii], 16, kWave);
+            const float p2 = __shfl_down(cc[ii], 32, kWave);
+            const int g = 4 * ps + ii;
+            if (g < G) sv[g] = valid ? cc[ii] + (p1 + p2) : -INFINITY;
+          }
+        }
+        float pv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float gm = __shfl(group_max<16>(sv[g]), 0, kWave);
+          pv[g] = 0.f;
+          if (gm > -INFINITY) {  // the group holds a valid token
+            const float mn = fmaxf(m[g], gm);
+            const float sc = expf(m[g] - mn);  // 0 while m is -inf
+            pv[g] = expf(sv[g] - mn);          // 0 for invalid tokens
+            const float ps = __shfl(group_sum<16>(pv[g]), 0, kWave);
+            l[g] = fmaf(l[g], sc, ps);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[g][j] *= sc;
+            m[g] = mn;
+          }
+        }
+#pragma unroll
+        for (int vi = 0; vi < NVI; ++vi) {
+          const int tl = vi * TPI + sub;  // token within the group
+          const int i2 = base + tl;
+          const int jj2 = i2 / P, t2 = i2 - jj2 * P;
+          const bool ok = i2 < npos && t2 < cp.nt[jj2 < kMaxChunkPages ? jj2 : 0];
+          float xv[8];
+          vv[e][vi].unpack(xv);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pw = __shfl(pv[g], tl, kWave);
+            if (ok) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(pw, xv[j], acc[g][j]);
+            }
+          }
+        }
+      }
+    }
+    // merge the wave's token subgroups (lanes with equal li), then the waves
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v = acc[g][j];
+#pragma unroll
+        for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+        acc[g][j] = v;
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) { s_m[wave][g] = m[g]; s_l[wave][g] = l[g]; }
+    }
+    if (sub == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
+    }
+    lds_barrier();
+    const size_t pc = static_cast<size_t>(u) * maxch + c;
+    for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
+      const int g = e / D, d = e % D;
+      float M = s_m[0][g];
+#pragma unroll
+      for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, s_m[ww][g]);
+      float o = 0.f, ls = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const float wt = s_m[ww][g] > -INFINITY ? expf(s_m[ww][g] - M) : 0.f;
+        o = fmaf(wt, s_acc[ww][g][d], o);
+        ls = fmaf(wt, s_l[ww][g], ls);
+      }
+      part_o[pc * G * D + e] = o;
+      if (d == 0) {
+        part_l[pc * G + g] = ls;
+        part_m[pc * G + g] = M;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// Merge: grid (units*G, D/kCombD); kCombSlices slices of chunks per block.
+constexpr int kCombD = 16;
+constexpr int kCombSlices = 64;
+
+__global__ __launch_bounds__(kCombD * kCombSlices) void k_softmax_combine(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, int H, int G, int D, int P, int maxch,
     const float *__restrict__ part_m, const float *__restrict__ part_l,
     const float *__restrict__ part_o, float *__restrict__ out,
     float *__restrict__ lse) {
-  __shared__ float red_f[kCombThreads / kWave];
-  __shared__ float s_o[kCombThreads];
-  __shared__ float s_l[kCombThreads];
-  const int ug = blockIdx.x, u = ug / G, g = ug % G, b = u / H;
+  constexpr int NT = kCombD * kCombSlices;
+  __shared__ float red_f[NT / kWave];
+  __shared__ float s_o[kCombSlices][kCombD];
+  __shared__ float s_l[kCombSlices];
+  const int ug = blockIdx.x, u = ug / G, g = ug % G;
   const int tid = threadIdx.x;
-  const int len = seq_lens[b];
-  const int cnt = sel ? count[u] : n_pages_of(len, P);
+  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   const int ppc = kChunkTokens / P;
   const int nch = (cnt + ppc - 1) / ppc;
+  const size_t ub = static_cast<size_t>(u) * maxch;
   float mloc = -FLT_MAX;
-  for (int c = tid; c < nch; c += kCombThreads)
-    mloc = fmaxf(mloc, part_m[(static_cast<size_t>(u) * maxch + c) * G + g]);
-  const float M = block_max<kCombThreads>(mloc, red_f);
-  const int slices = kCombThreads / D;
-  const int d = tid % D, sl = tid / D;
+  for (int c = tid; c < nch; c += NT) mloc = fmaxf(mloc, part_m[(ub + c) * G + g]);
+  const float M = block_max<NT>(mloc, red_f);
+  const int dl = tid % kCombD, sl = tid / kCombD;
+  const int d = blockIdx.y * kCombD + dl;
   float o = 0.f, l = 0.f;
-  if (sl < slices) {
-    for (int c = sl; c < nch; c += slices) {
-      const size_t base = (static_cast<size_t>(u) * maxch + c) * G + g;
-      const float w = expf(part_m[base] - M);
-      o = fmaf(w, part_o[base * D + d], o);
-      if (d == 0) l = fmaf(w, part_l[base], l);
-    }
+#pragma unroll 4
+  for (int c = sl; c < nch; c += kCombSlices) {
+    const size_t base = (ub + c) * G + g;
+    const float wgt = expf(part_m[base] - M);
+    o = fmaf(wgt, part_o[base * D + d], o);
+    l = fmaf(wgt, part_l[base], l);
   }
-  s_o[tid] = o;
-  s_l[tid] = l;
-  __syncthreads();
-  if (tid < D) {
+  s_o[sl][dl] = o;
+  if (dl == 0) s_l[sl] = l;
+  lds_barrier();
+  if (tid < kCombD) {
     float oo = 0.f, ll = 0.f;
-    for (int k = 0; k < slices; ++k) {
-      oo += s_o[k * D + tid];
-      ll += s_l[k * D];
+    for (int k = 0; k < kCombSlices; ++k) {
+      oo += s_o[k][tid];
+      ll += s_l[k];
     }
-    out[static_cast<size_t>(ug) * D + tid] = oo / ll;
-    if (lse && tid == 0) lse[ug] = M + logf(ll);
+    out[static_cast<size_t>(ug) * D + blockIdx.y * kCombD + tid] = oo / ll;
+    if (lse && blockIdx.y == 0 && tid == 0) lse[ug] = M + logf(ll);
   }
 }
 
@@ -877,6 +1516,18 @@ static inline int exponent_code(float alpha, float &rg) {
   return 0;
 }
 
+// Persistent grid: enough blocks to fill the device, never more than items.
+static int persistent_blocks(size_t max_items, int per_cu) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  const size_t cap = static_cast<size_t>(n_cu) * per_cu;
+  if (max_items == 0) return 1;
+  return static_cast<int>(max_items < cap ? max_items : cap);
+}
+
 template <class E, int D, int G>
 hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 float scale, float alpha, const int32_t *sel,
@@ -884,15 +1535,42 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 hipStream_t stream) {
   const DecodeWs L = decode_ws_layout(kv);
   char *w = static_cast<char *>(ws);
-  const int mc = max_chunks(kv);
-  dim3 grid(mc, kv.batch * kv.num_kv_heads);
-  hipLaunchKernelGGL((k_entmax_scores<E, D, G>), grid, dim3(kDecThreads), 0,
-                     stream, static_cast<const typename E::T *>(kv.k),
-                     kv.page_table, kv.seq_lens, sel, count, q,
-                     (alpha - 1.0f) * scale, kv.num_kv_heads, kv.page_size,
-                     kv.max_pages, kv.max_pages * kv.page_size, mc,
-                     reinterpret_cast<float *>(w + L.z),
-                     reinterpret_cast<float *>(w + L.cmax));
+  const int units = kv.batch * kv.num_kv_heads;
+  const size_t pages = static_cast<size_t>(units) * kv.max_pages;
+  const int blocks = persistent_blocks((pages + kDecWaves - 1) / kDecWaves, 8);
+  const int cap = kv.max_pages * kv.page_size;
+  float *z = reinterpret_cast<float *>(w + L.z);
+  float *pm = reinterpret_cast<float *>(w + L.cmax);
+  const float zs = (alpha - 1.0f) * scale;
+  if constexpr (sizeof(typename E::T) == 2) {
+    const uint16_t *k = static_cast<const uint16_t *>(kv.k);
+    switch (kv.page_size) {
+      case 16:
+        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 16>), dim3(blocks),
+                           dim3(kDecThreads), 0, stream, k, kv.page_table,
+                           kv.seq_lens, sel, count, q, zs, units,
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+        break;
+      case 32:
+        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 32>), dim3(blocks),
+                           dim3(kDecThreads), 0, stream, k, kv.page_table,
+                           kv.seq_lens, sel, count, q, zs, units,
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+        break;
+      default:
+        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 64>), dim3(blocks),
+                           dim3(kDecThreads), 0, stream, k, kv.page_table,
+                           kv.seq_lens, sel, count, q, zs, units,
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+        break;
+    }
+  } else {
+    hipLaunchKernelGGL((k_entmax_scores_valu<E, D, G>), dim3(blocks),
+                       dim3(kDecThreads), 0, stream,
+                       static_cast<const typename E::T *>(kv.k), kv.page_table,
+                       kv.seq_lens, sel, count, q, zs, units, kv.num_kv_heads,
+                       kv.page_size, kv.max_pages, cap, z, pm);
+  }
   return hipGetLastError();
 }
 
@@ -909,7 +1587,7 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<const float *>(w + L.z),
                      reinterpret_cast<const float *>(w + L.cmax), kv.seq_lens,
                      sel, count, kv.num_kv_heads, G, kv.page_size,
-                     kv.max_pages * kv.page_size, max_chunks(kv), r, rg,
+                     kv.max_pages, kv.max_pages * kv.page_size, r, rg,
                      reinterpret_cast<float *>(w + L.tau), tau);
   return hipGetLastError();
 }
@@ -932,12 +1610,13 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
     hipLaunchKernelGGL(k_fill_probs, g, dim3(256), 0, stream, kv.seq_lens,
                        kv.num_kv_heads * G, pstride, probs);
   }
-  hipLaunchKernelGGL((k_entmax_apply<E, D, G>), dim3(mc, units),
+  const int blocks = persistent_blocks(static_cast<size_t>(units) * mc, 4);
+  hipLaunchKernelGGL((k_entmax_apply<E, D, G>), dim3(blocks),
                      dim3(kDecThreads), 0, stream,
                      static_cast<const typename E::T *>(kv.v), kv.page_table,
-                     kv.seq_lens, sel, count, kv.num_kv_heads, kv.page_size,
-                     kv.max_pages, kv.max_pages * kv.page_size, mc, r, rg,
-                     reinterpret_cast<const float *>(w + L.z),
+                     kv.seq_lens, sel, count, units, kv.num_kv_heads,
+                     kv.page_size, kv.max_pages, kv.max_pages * kv.page_size,
+                     mc, r, rg, reinterpret_cast<const float *>(w + L.z),
                      reinterpret_cast<const float *>(w + L.cmax),
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<float *>(w + L.part_o),
@@ -946,7 +1625,7 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_entmax_combine, dim3(units * G), dim3(kCombThreads), 0,
                      stream, kv.seq_lens, sel, count, kv.num_kv_heads, G, D,
-                     kv.page_size, mc,
+                     kv.page_size, kv.max_pages, mc,
                      reinterpret_cast<const float *>(w + L.cmax),
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<const float *>(w + L.part_o),
@@ -962,20 +1641,32 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
   char *w = static_cast<char *>(ws);
   const int mc = max_chunks(kv);
   const int units = kv.batch * kv.num_kv_heads;
-  hipLaunchKernelGGL((k_softmax_partial<E, D, G>), dim3(mc, units),
+  const int blocks = persistent_blocks(static_cast<size_t>(units) * mc, 4);
+  if constexpr (sizeof(typename E::T) == 2) {
+    hipLaunchKernelGGL((k_softmax_partial_mfma<D, G>), dim3(blocks),
+                       dim3(kDecThreads), 0, stream,
+                       static_cast<const uint16_t *>(kv.k),
+                       static_cast<const uint16_t *>(kv.v), kv.page_table,
+                       kv.seq_lens, sel, count, q, scale, units,
+                       kv.num_kv_heads, kv.page_size, kv.max_pages, mc,
+                       reinterpret_cast<float *>(w + L.part_m),
+                       reinterpret_cast<float *>(w + L.part_l),
+                       reinterpret_cast<float *>(w + L.part_o));
+  } else
+  hipLaunchKernelGGL((k_softmax_partial<E, D, G>), dim3(blocks),
                      dim3(kDecThreads), 0, stream,
                      static_cast<const typename E::T *>(kv.k),
                      static_cast<const typename E::T *>(kv.v), kv.page_table,
-                     kv.seq_lens, sel, count, q, scale, kv.num_kv_heads,
+                     kv.seq_lens, sel, count, q, scale, units, kv.num_kv_heads,
                      kv.page_size, kv.max_pages, mc,
                      reinterpret_cast<float *>(w + L.part_m),
                      reinterpret_cast<float *>(w + L.part_l),
                      reinterpret_cast<float *>(w + L.part_o));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_softmax_combine, dim3(units * G), dim3(kCombThreads), 0,
-                     stream, kv.seq_lens, sel, count, kv.num_kv_heads, G, D,
-                     kv.page_size, mc,
+  hipLaunchKernelGGL(k_softmax_combine, dim3(units * G, D / kCombD),
+                     dim3(kCombD * kCombSlices), 0, stream, kv.seq_lens, sel,
+                     count, kv.num_kv_heads, G, D, kv.page_size, mc,
                      reinterpret_cast<const float *>(w + L.part_m),
                      reinterpret_cast<const float *>(w + L.part_l),
                      reinterpret_cast<const float *>(w + L.part_o), out, lse);

@@ -60,17 +60,41 @@ __device__ __forceinline__ void store1(uint16_t *p, float x) {
 // ---------------------------------------------------------------------------
 // Lane-group reductions.  W lanes (power of two, <= 64) that are contiguous
 // and W-aligned reduce to a value present in every lane of the group.
+// Within a row of 16 lanes the data-parallel-primitive (DPP) lane swizzles
+// are used: row_mirror pairs lane i with 15-i, row_half_mirror pairs i with
+// 7-i inside each half row, and the two quad permutations exchange
+// neighbours and pairs; across rows the cross-lane shuffle is used.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppQuad1032 = 0xB1;  // quad_perm(1, 0, 3, 2)
+constexpr int kDppQuad2301 = 0x4E;  // quad_perm(2, 3, 0, 1)
+
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two");
+  if constexpr (W >= 16) x += dpp_f<kDppRowMirror>(x);
+  if constexpr (W >= 8) x += dpp_f<kDppRowHalfMirror>(x);
+  if constexpr (W >= 4) x += dpp_f<kDppQuad2301>(x);
+  if constexpr (W >= 2) x += dpp_f<kDppQuad1032>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, kWave);
   return x;
 }
 template <int W>
 __device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two");
+  if constexpr (W >= 16) x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  if constexpr (W >= 8) x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  if constexpr (W >= 4) x = fmaxf(x, dpp_f<kDppQuad2301>(x));
+  if constexpr (W >= 2) x = fmaxf(x, dpp_f<kDppQuad1032>(x));
+  if constexpr (W >= 32) x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  if constexpr (W >= 64) x = fmaxf(x, __shfl_xor(x, 32, kWave));
   return x;
 }
 template <int W>
@@ -84,6 +108,15 @@ __device__ __forceinline__ int group_sum_i(int x) {
 #pragma unroll
   for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
   return x;
+}
+
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
+// it does not wait for outstanding global loads, so loads issued before it
+// stay in flight.  Use it wherever threads exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -105,9 +138,9 @@ __device__ __forceinline__ int block_excl_scan(int x, int *smem, int &total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int incl = wave_incl_scan(x);
-  __syncthreads();
+  lds_barrier();
   if (lane == kWave - 1) smem[wid] = incl;
-  __syncthreads();
+  lds_barrier();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -125,9 +158,9 @@ template <int NT>
 __device__ __forceinline__ float block_max(float x, float *smem) {
   constexpr int NW = NT / kWave;
   x = group_max<kWave>(x);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
-  __syncthreads();
+  lds_barrier();
   float r = smem[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = fmaxf(r, smem[w]);
@@ -137,9 +170,9 @@ template <int NT>
 __device__ __forceinline__ double block_sum_d(double x, double *smem) {
   constexpr int NW = NT / kWave;
   x = group_sum_d<kWave>(x);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
-  __syncthreads();
+  lds_barrier();
   double r = smem[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r += smem[w];
@@ -149,13 +182,38 @@ template <int NT>
 __device__ __forceinline__ int block_sum_i(int x, int *smem) {
   constexpr int NW = NT / kWave;
   x = group_sum_i<kWave>(x);
-  __syncthreads();
+  lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
-  __syncthreads();
+  lds_barrier();
   int r = smem[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r += smem[w];
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// Ordered compaction of one tile of NT flags (one per thread): returns the
+// flag's rank among the set flags of the tile (in thread order) and the
+// tile's total.  `smem` holds NT/64 ints.  Contains barriers.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ int tile_rank(bool flag, int *smem, int &total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const unsigned long long ball = __ballot(flag);
+  const int below = __popcll(ball & ((1ull << lane) - 1ull));
+  lds_barrier();
+  if (lane == 0) smem[wid] = __popcll(ball);
+  lds_barrier();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int v = smem[w];
+    base += (w < wid) ? v : 0;
+    tot += v;
+  }
+  total = tot;
+  return base + below;
 }
 
 // ---------------------------------------------------------------------------

@@ -11,6 +11,21 @@ namespace ekv {
 struct F32;
 struct BF16;
 
+// Pages summarised together by the scoring kernel (one tile per block).
+constexpr int kPageTile = 64;
+
+// Float offset of the Gaussian tile summaries in gstat: after the per-page
+// (mu, sigma^2) pairs, rounded up to 4 floats so the float4 rows are aligned.
+__host__ __device__ inline size_t gstat_tile_offset(int batch, int Hq,
+                                                    int max_pages) {
+  const size_t n = static_cast<size_t>(batch) * Hq * max_pages * 2;
+  return (n + 3) & ~static_cast<size_t>(3);
+}
+
+inline int page_tiles(const ekv_paged_kv &kv) {
+  return (kv.max_pages + kPageTile - 1) / kPageTile;
+}
+
 // Tokens covered by one decode work item (a "chunk" of selected pages).
 constexpr int kChunkTokens = 512;
 
@@ -65,6 +80,9 @@ template <class E, int D, int G>
 hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
                           const int32_t *sel, const int32_t *count, float *out,
                           float *lse, void *ws, hipStream_t stream);
+
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                             hipStream_t stream);
 
 #define EKV_FOR_EACH_G(X) X(1) X(2) X(4) X(8)
 #define EKV_FOR_EACH_ED(X) X(F32, 64) X(F32, 128) X(BF16, 64) X(BF16, 128)

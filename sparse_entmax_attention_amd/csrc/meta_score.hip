@@ -6,97 +6,137 @@
 // from cache) and writes 2*D box values and 2*D float32 moments; scoring
 // reads those records back and writes G floats (box) or G float pairs
 // (Gaussian) per record.  Both are HBM-bound.
+#include <float.h>
+
 #include "ekv_device.h"
 #include "ekv_kernels.h"
 
 namespace ekv {
 
 // ---------------------------------------------------------------------------
-// Metadata build: one wave per (sequence, logical page, KV head).  Lanes own
-// D/64 coordinates; tokens are walked in order so every page's result is a
-// fixed function of its keys (an incremental refresh equals a full build).
+// Metadata build: one block per (sequence, logical page, KV head).  Thread
+// (tg, cg) loads coordinates 8cg..8cg+7 of tokens tg, tg+TG, ... (16-byte
+// loads, the whole page in flight at once) and keeps partial minima, maxima
+// and sums; the TG partials of each coordinate are combined in a fixed
+// order, so every page's result is a fixed function of its keys and an
+// incremental refresh equals a full build bit for bit.  The variance is
+// taken about the mean in a second pass over the registers.
 // ---------------------------------------------------------------------------
+constexpr int kMetaThreads = 256;
+
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_build_meta(
+__global__ __launch_bounds__(kMetaThreads) void k_build_meta(
     const typename E::T *__restrict__ kpool,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ first_page, int H, int P, int max_pages,
     typename E::T *__restrict__ bbox, float *__restrict__ gauss) {
-  constexpr int CPL = D / kWave;  // coordinates per lane
+  constexpr int CG = D / 8;                 // coordinate groups
+  constexpr int TG = kMetaThreads / CG;     // token groups
+  constexpr int MAXT = (64 + TG - 1) / TG;  // tokens per thread (P <= 64)
+  __shared__ float s_a[TG][D];
+  __shared__ float s_b[TG][D];
+  __shared__ float s_c[TG][D];
+  __shared__ float s_mean[D];
   const int b = blockIdx.z, h = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int cg = threadIdx.x % CG, tg = threadIdx.x / CG, d0 = cg * 8;
   const int len = seq_lens[b];
   const int np = n_pages_of(len, P);
   int p0 = first_page ? first_page[b] : 0;
   if (p0 < 0) p0 = 0;
-  constexpr int kWavesPerBlock = 4;
-  for (int lp = p0 + blockIdx.x * kWavesPerBlock + wave; lp < np;
-       lp += gridDim.x * kWavesPerBlock) {
-    const int slot = page_table[b * max_pages + lp];
+  for (int lp = p0 + blockIdx.x; lp < np; lp += gridDim.x) {
+    const int slot = page_table[static_cast<size_t>(b) * max_pages + lp];
     const int n = page_tokens(lp, len, P);
     const typename E::T *base = kpool + pool_row(slot, h, 0, H, P, D);
-    float mn[CPL], mx[CPL], sm[CPL];
+    float x[MAXT][8];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float x = load1(base + lane * CPL + c);
-      mn[c] = x; mx[c] = x; sm[c] = x;
+    for (int i = 0; i < MAXT; ++i) {
+      const int t = tg + i * TG;
+      if (t < n) load8(base + static_cast<size_t>(t) * D + d0, x[i]);
     }
-    for (int t = 1; t < n; ++t) {
+    float mn[8], mx[8], sm[8];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float x = load1(base + static_cast<size_t>(t) * D + lane * CPL + c);
-        mn[c] = fminf(mn[c], x);
-        mx[c] = fmaxf(mx[c], x);
-        sm[c] += x;
-      }
-    }
-    if (bbox) {
+    for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; sm[j] = 0.f; }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        store1(bbox + meta_row(slot, h, 0, H, D) + lane * CPL + c, mn[c]);
-        store1(bbox + meta_row(slot, h, 1, H, D) + lane * CPL + c, mx[c]);
-      }
-    }
-    if (gauss) {
-      float mean[CPL], ss[CPL];
+    for (int i = 0; i < MAXT; ++i)
+      if (tg + i * TG < n)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        mean[c] = sm[c] / static_cast<float>(n);
-        ss[c] = 0.f;
-      }
-      for (int t = 0; t < n; ++t) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float x = load1(base + static_cast<size_t>(t) * D + lane * CPL + c);
-          const float dv = x - mean[c];
-          ss[c] = fmaf(dv, dv, ss[c]);
+        for (int j = 0; j < 8; ++j) {
+          mn[j] = fminf(mn[j], x[i][j]);
+          mx[j] = fmaxf(mx[j], x[i][j]);
+          sm[j] += x[i][j];
         }
-      }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        gauss[meta_row(slot, h, 0, H, D) + lane * CPL + c] = mean[c];
-        gauss[meta_row(slot, h, 1, H, D) + lane * CPL + c] =
-            ss[c] / static_cast<float>(n);
+    for (int j = 0; j < 8; ++j) {
+      s_a[tg][d0 + j] = mn[j];
+      s_b[tg][d0 + j] = mx[j];
+      s_c[tg][d0 + j] = sm[j];
+    }
+    lds_barrier();
+    if (threadIdx.x < D) {
+      const int d = threadIdx.x;
+      float a = s_a[0][d], c = s_b[0][d], s = s_c[0][d];
+      for (int k = 1; k < TG; ++k) {
+        a = fminf(a, s_a[k][d]);
+        c = fmaxf(c, s_b[k][d]);
+        s += s_c[k][d];
+      }
+      const float mean = s / static_cast<float>(n);
+      s_mean[d] = mean;
+      if (bbox) {
+        store1(bbox + meta_row(slot, h, 0, H, D) + d, a);
+        store1(bbox + meta_row(slot, h, 1, H, D) + d, c);
+      }
+      if (gauss) gauss[meta_row(slot, h, 0, H, D) + d] = mean;
+    }
+    lds_barrier();
+    if (gauss) {
+      float ss[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXT; ++i)
+        if (tg + i * TG < n)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float dv = x[i][j] - s_mean[d0 + j];
+            ss[j] = fmaf(dv, dv, ss[j]);
+          }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_c[tg][d0 + j] = ss[j];
+      lds_barrier();
+      if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        float s = s_c[0][d];
+        for (int k = 1; k < TG; ++k) s += s_c[k][d];
+        gauss[meta_row(slot, h, 1, H, D) + d] = s / static_cast<float>(n);
       }
     }
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
+// Page scoring.  Besides the per-page values the kernel writes, for every
+// 64-page tile (one block), summaries the selectors use to skip tiles:
+//   box:       max over the tile's pages and the group's heads of the bound;
+//   Gaussian:  per query head max mu, max (mu + 8.5 sigma) and
+//              max (mu + sqrt(2 ln P) sigma).
+// They live after the per-page values in the same buffers (see entmaxkv.h).
+//
 // Page scoring: D/8 lanes per page (8 coordinates per lane, 16-byte loads of
 // bf16 box values), 64*8/D pages per wave step.  The box bound uses
 // max(q kmin, q kmax) = q+ kmax + q- kmin per coordinate (q+ = max(q, 0),
 // q- = min(q, 0)): the same rounded product is picked either way.
 // ---------------------------------------------------------------------------
-constexpr int kScoreTile = 64;  // pages per block
+constexpr int kScoreTile = kPageTile;  // pages per block
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(256) void k_score(
     const typename E::T *__restrict__ bbox, const float *__restrict__ gauss,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const float *__restrict__ q,
-    float scale, int mode, int H, int P, int max_pages,
+    float scale, int mode, int H, int P, int max_pages, int batch,
     float *__restrict__ ub, float *__restrict__ gstat) {
   constexpr int LPP = D / 8;          // lanes per page
   constexpr int PPW = kWave / LPP;    // pages per wave step
@@ -110,6 +150,8 @@ __global__ __launch_bounds__(256) void k_score(
   const int tile0 = blockIdx.x * kScoreTile;
   if (tile0 >= np) return;
   const int Hq = H * G;
+  const int n_tiles = (max_pages + kScoreTile - 1) / kScoreTile;
+  __shared__ float s_tile[4][3 * G + 1];
 
   float qp[G][8], qn[G][8];
 #pragma unroll
@@ -123,46 +165,80 @@ __global__ __launch_bounds__(256) void k_score(
     }
   }
 
-  for (int i = wave * PPW + sub; i < kScoreTile; i += NWAVE * PPW) {
-    const int lp = tile0 + i;
-    const bool valid = lp < np;
-    const int slot = valid ? page_table[b * max_pages + lp] : 0;
-    if (mode & EKV_SCORE_BBOX) {
-      float kmin[8], kmax[8];
-      if (valid) {
-        load8(bbox + meta_row(slot, h, 0, H, D) + d0, kmin);
-        load8(bbox + meta_row(slot, h, 1, H, D) + d0, kmax);
+  constexpr int NSTEP = kScoreTile / (NWAVE * PPW);
+  int lps[NSTEP], slots[NSTEP];
+  bool valid[NSTEP];
+#pragma unroll
+  for (int k = 0; k < NSTEP; ++k) {
+    lps[k] = tile0 + (k * NWAVE + wave) * PPW + sub;
+    valid[k] = lps[k] < np;
+    slots[k] = valid[k] ? page_table[b * max_pages + lps[k]] : 0;
+  }
+  if (mode & EKV_SCORE_BBOX) {
+    float tmax = -FLT_MAX;
+    float kmin[NSTEP][8], kmax[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      if (valid[k]) {
+        load8(bbox + meta_row(slots[k], h, 0, H, D) + d0, kmin[k]);
+        load8(bbox + meta_row(slots[k], h, 1, H, D) + d0, kmax[k]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { kmin[j] = 0.f; kmax[j] = 0.f; }
+        for (int j = 0; j < 8; ++j) { kmin[k][j] = 0.f; kmax[k][j] = 0.f; }
       }
+    }
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
       float acc[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float a = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          a = fmaf(qp[g][j], kmax[j], a);
-          a = fmaf(qn[g][j], kmin[j], a);
+          a = fmaf(qp[g][j], kmax[k][j], a);
+          a = fmaf(qn[g][j], kmin[k][j], a);
         }
         acc[g] = group_sum<LPP>(a);
       }
-      if (valid) {
+      if (valid[k]) {
+        float gm = acc[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) gm = fmaxf(gm, acc[g]);
+        tmax = fmaxf(tmax, gm);
 #pragma unroll
         for (int g = 0; g < G; ++g)
           if (li == g)
-            ub[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lp] = acc[g];
+            ub[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lps[k]] = acc[g];
       }
     }
-    if (mode & EKV_SCORE_GAUSS) {
-      float mean[8], var[8];
-      if (valid) {
-        load8(gauss + meta_row(slot, h, 0, H, D) + d0, mean);
-        load8(gauss + meta_row(slot, h, 1, H, D) + d0, var);
+    tmax = group_max<kWave>(tmax);
+    if (lane == 0) s_tile[wave][3 * G] = tmax;
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      float m = s_tile[0][3 * G];
+      for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, s_tile[w][3 * G]);
+      ub[static_cast<size_t>(batch) * Hq * max_pages +
+         (static_cast<size_t>(b) * H + h) * n_tiles + blockIdx.x] = m;
+    }
+  }
+  if (mode & EKV_SCORE_GAUSS) {
+    const float cP = sqrtf(2.0f * logf(static_cast<float>(P)));
+    float t_mu[G], t_pr[G], t_kp[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) { t_mu[g] = -FLT_MAX; t_pr[g] = -FLT_MAX; t_kp[g] = -FLT_MAX; }
+    float mean[NSTEP][8], var[NSTEP][8];
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      if (valid[k]) {
+        load8(gauss + meta_row(slots[k], h, 0, H, D) + d0, mean[k]);
+        load8(gauss + meta_row(slots[k], h, 1, H, D) + d0, var[k]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { mean[j] = 0.f; var[j] = 0.f; }
+        for (int j = 0; j < 8; ++j) { mean[k][j] = 0.f; var[k][j] = 0.f; }
       }
+    }
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
       float mu[G], s2[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -170,22 +246,55 @@ __global__ __launch_bounds__(256) void k_score(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float x = qp[g][j] + qn[g][j];
-          a = fmaf(x, mean[j], a);
-          c = fmaf(x * x, var[j], c);
+          a = fmaf(x, mean[k][j], a);
+          c = fmaf(x * x, var[k][j], c);
         }
         mu[g] = group_sum<LPP>(a);
         s2[g] = group_sum<LPP>(c);
       }
-      if (valid) {
+      if (valid[k]) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+          const float sd = sqrtf(fmaxf(s2[g], 0.f));
+          t_mu[g] = fmaxf(t_mu[g], mu[g]);
+          t_pr[g] = fmaxf(t_pr[g], mu[g] + 8.5f * sd);
+          t_kp[g] = fmaxf(t_kp[g], mu[g] + cP * sd);
           if (li == g) {
-            float2 r;
-            r.x = mu[g];
-            r.y = s2[g];
-            reinterpret_cast<float2 *>(gstat)[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lp] = r;
+            float2 rr;
+            rr.x = mu[g];
+            rr.y = s2[g];
+            reinterpret_cast<float2 *>(gstat)[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lps[k]] = rr;
           }
+        }
       }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float a0 = group_max<kWave>(t_mu[g]);
+      const float a1 = group_max<kWave>(t_pr[g]);
+      const float a2 = group_max<kWave>(t_kp[g]);
+      if (lane == 0) {
+        s_tile[wave][3 * g] = a0;
+        s_tile[wave][3 * g + 1] = a1;
+        s_tile[wave][3 * g + 2] = a2;
+      }
+    }
+    lds_barrier();
+    if (threadIdx.x < G) {
+      const int g = threadIdx.x;
+      float4 r4;
+      r4.x = s_tile[0][3 * g];
+      r4.y = s_tile[0][3 * g + 1];
+      r4.z = s_tile[0][3 * g + 2];
+      r4.w = 0.f;
+      for (int w = 1; w < NWAVE; ++w) {
+        r4.x = fmaxf(r4.x, s_tile[w][3 * g]);
+        r4.y = fmaxf(r4.y, s_tile[w][3 * g + 1]);
+        r4.z = fmaxf(r4.z, s_tile[w][3 * g + 2]);
+      }
+      float4 *gt = reinterpret_cast<float4 *>(
+          gstat + gstat_tile_offset(batch, Hq, max_pages));
+      gt[(static_cast<size_t>(b) * Hq + h * G + g) * n_tiles + blockIdx.x] = r4;
     }
   }
 }
@@ -198,8 +307,8 @@ hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
                              int span, const ekv_meta &meta,
                              hipStream_t stream) {
   const int pages = span > 0 && span < kv.max_pages ? span : kv.max_pages;
-  dim3 grid((pages + 3) / 4, kv.num_kv_heads, kv.batch);
-  hipLaunchKernelGGL((k_build_meta<E, D>), grid, dim3(256), 0, stream,
+  dim3 grid(pages, kv.num_kv_heads, kv.batch);
+  hipLaunchKernelGGL((k_build_meta<E, D>), grid, dim3(kMetaThreads), 0, stream,
                      static_cast<const typename E::T *>(kv.k), kv.page_table,
                      kv.seq_lens, first_page, kv.num_kv_heads, kv.page_size,
                      kv.max_pages, static_cast<typename E::T *>(meta.bbox),
@@ -216,7 +325,8 @@ hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
   hipLaunchKernelGGL((k_score<E, D, G>), grid, dim3(256), 0, stream,
                      static_cast<const typename E::T *>(meta.bbox), meta.gauss,
                      kv.page_table, kv.seq_lens, q, scale, mode,
-                     kv.num_kv_heads, kv.page_size, kv.max_pages, ub, gstat);
+                     kv.num_kv_heads, kv.page_size, kv.max_pages, kv.batch, ub,
+                     gstat);
   return hipGetLastError();
 }
 

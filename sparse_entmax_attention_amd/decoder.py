@@ -29,8 +29,17 @@ class DecodeBuffers:
         self.scale = 1.0 / math.sqrt(D)
         self.bbox = torch.empty(S, H, 2, D, dtype=kv.k.dtype, device=dev) if bbox else None
         self.gauss = torch.empty(S, H, 2, D, dtype=torch.float32, device=dev) if gauss else None
-        self.ub = torch.empty(Bt, Hq, MP, dtype=torch.float32, device=dev) if bbox else None
-        self.gstat = torch.empty(Bt, Hq, MP, 2, dtype=torch.float32, device=dev) if gauss else None
+        # ub / gstat hold the per-page values followed by 64-page tile
+        # summaries; .ub and .gstat are views of the per-page part.
+        self.ub_buf = self.ub = self.gstat_buf = self.gstat = None
+        if bbox:
+            self.ub_buf = torch.empty(B.ekv_score_size(kv, B.EKV_SCORE_BBOX),
+                                      dtype=torch.float32, device=dev)
+            self.ub = self.ub_buf[:Bt * Hq * MP].view(Bt, Hq, MP)
+        if gauss:
+            self.gstat_buf = torch.empty(B.ekv_score_size(kv, B.EKV_SCORE_GAUSS),
+                                         dtype=torch.float32, device=dev)
+            self.gstat = self.gstat_buf[:Bt * Hq * MP * 2].view(Bt, Hq, MP, 2)
         self.sel = torch.empty(Bt, H, MP, dtype=torch.int32, device=dev)
         self.count = torch.empty(Bt, H, dtype=torch.int32, device=dev)
         self.tau_hat = torch.empty(Bt, Hq, dtype=torch.float32, device=dev)
@@ -55,16 +64,16 @@ class DecodeBuffers:
 
     def score(self, q, mode: int, stream=None):
         B.ekv_score_pages(self.kv, self.bbox, self.gauss, q, self.scale, mode,
-                          self.ub if mode & B.EKV_SCORE_BBOX else None,
-                          self.gstat if mode & B.EKV_SCORE_GAUSS else None,
+                          self.ub_buf if mode & B.EKV_SCORE_BBOX else None,
+                          self.gstat_buf if mode & B.EKV_SCORE_GAUSS else None,
                           stream)
 
     def select_topk(self, k: int, stream=None):
-        B.ekv_select_topk(self.kv, self.ub, k, self.sel, self.count,
+        B.ekv_select_topk(self.kv, self.ub_buf, k, self.sel, self.count,
                           self.ws_topk, stream)
 
     def select_gauss(self, alpha: float, delta: float, stream=None):
-        B.ekv_select_gauss(self.kv, self.gstat, alpha, delta, self.sel,
+        B.ekv_select_gauss(self.kv, self.gstat_buf, alpha, delta, self.sel,
                            self.count, self.tau_hat, self.ws_gauss, stream)
 
     def entmax(self, q, alpha: float, selected: bool = True, probs=None,

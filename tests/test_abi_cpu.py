@@ -66,6 +66,13 @@ def test_workspace_sizes(lib):
     topk = lib.ekv_workspace_size(B.EKV_OP_SELECT_TOPK, ctypes.byref(kv), 16)
     assert topk >= units * 1024 * 4
     assert lib.ekv_workspace_size(99, ctypes.byref(kv), 0) == 0
+    # score buffers: per-page values plus 64-page tile summaries
+    T = (1024 + 63) // 64
+    assert lib.ekv_score_size(ctypes.byref(kv), B.EKV_SCORE_BBOX) == 32 * 1024 + 8 * T
+    assert lib.ekv_score_size(ctypes.byref(kv), B.EKV_SCORE_GAUSS) == 32 * 1024 * 2 + 32 * T * 4
+    odd = _kv(num_kv_heads=1, group=1, max_pages=5)  # tile rows start 4-aligned
+    assert lib.ekv_score_size(ctypes.byref(odd), B.EKV_SCORE_GAUSS) == 12 + 4
+    assert lib.ekv_score_size(ctypes.byref(kv), 3) == 0
     bad = _kv(head_dim=96)
     assert lib.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE, ctypes.byref(bad), 0) == 0
 

@@ -115,12 +115,13 @@ def test_page_scores(gpu, name):
             assert (np.abs(gstat[b, h * G + g, :n, 1] - s2) <= 1e-4 * s2 + 1e-6).all()
 
 
-@pytest.mark.parametrize("name", ["needle4k_f32_d64", "needle32k_gqa", "cluster_p64"])
+@pytest.mark.parametrize("name,k", [("needle4k_f32_d64", 32), ("needle32k_gqa", 32),
+                                    ("needle32k_gqa", 3), ("cluster_p64", 16),
+                                    ("cluster_p64", 200)])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
-def test_topk_decode(gpu, name, alpha):
+def test_topk_decode(gpu, name, k, alpha):
     inp, host = inputs(name, gpu)
     spec = inp.spec
-    k = spec.topk or 32
     kv = paged_kv(inp)
     buf = ekv.DecodeBuffers(kv)
     buf.build_meta()
@@ -328,3 +329,32 @@ def test_edge_cases(gpu):
     assert abs(f64(buf.tau_hat)[0, 0] - th) <= TAU_ATOL
     assert int(buf.count[0, 0]) == 1
     assert int(buf.sel[0, 0, 0]) == 0
+
+
+def test_topk_ties_across_tiles(gpu):
+    # Every page holds the same keys, so every box bound ties: the k pages
+    # kept must be the k lowest page indices, across 64-page tiles.
+    D, P, npg, k = 128, 32, 300, 70
+    print("[case] top-k ties", flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(11)
+    page = torch.randn(P, D, generator=g)
+    kk = page.repeat(npg, 2, 1, 1).reshape(npg, 2, P, D).to(torch.bfloat16).to(gpu)
+    vv = torch.randn(npg, 2, P, D, generator=g).to(torch.bfloat16).to(gpu)
+    pt = torch.arange(npg, dtype=torch.int32, device=gpu).reshape(1, npg)
+    sl = torch.tensor([npg * P - 7], dtype=torch.int32, device=gpu)
+    q = torch.randn(1, 4, D, generator=g).to(gpu)
+    buf = ekv.DecodeBuffers(ekv.PagedKV(kk, vv, pt, sl, 2))
+    buf.build_meta()
+    buf.step_topk(q, 1.5, k)
+    torch.cuda.synchronize()
+    # the last page is short: its box can differ, so rank it with the oracle
+    keys = f64(kk[:, 0]).reshape(-1, D)[:npg * P - 7]
+    kmin, kmax, _, _ = O.unit_metadata(keys, P)
+    qs = f64(q)[0]
+    for h in range(2):
+        gmax = np.max([O.bbox_bound(qs[h * 2 + j], kmin, kmax, 1 / math.sqrt(D))
+                       for j in range(2)], axis=0)
+        want = list(O.select_topk(gmax, k))
+        assert int(buf.count[0, h]) == k
+        assert list(buf.sel[0, h, :k].cpu().numpy()) == want
