@@ -42,8 +42,9 @@ def parse():
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache flush between timed steps (outside the events): "
                          "read a 1 GiB buffer (default), write 512 MiB, or none")
-    ap.add_argument("--cpu-units", type=int, default=1,
-                    help="(sequence, KV head) units the oracle is timed on; 0 skips")
+    ap.add_argument("--cpu-units", type=int, default=-1,
+                    help="(sequence, KV head) units the oracle is timed on; "
+                         "-1 (default) all units of one step, 0 skips")
     ap.add_argument("--legs", default="gauss,topk,entmax_full,softmax_full")
     return ap.parse_args()
 
@@ -103,6 +104,11 @@ def main():
     probe_ms = statistics.median(pe[2 * i].elapsed_time(pe[2 * i + 1]) for i in range(1, 6))
     read_probe_gbps = probe.numel() * 4 / (probe_ms * 1e-3) / 1e9
     del probe, sink
+    # A write of known size (256 MiB), the reference for hardware write counters.
+    calib = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    calib.fill_(1.0)
+    torch.cuda.synchronize()
+    del calib
 
     # Full metadata build (once; timed on its own).
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -267,8 +273,9 @@ def main():
                 results[base]["median_ms"] / results["topk"]["median_ms"], 3)
 
     cpu = None
-    if args.cpu_units > 0:
-        cpu = cpu_baseline(inp, spec, args.cpu_units, alpha, delta, log)
+    n_cpu = B * H if args.cpu_units < 0 else args.cpu_units
+    if n_cpu > 0:
+        cpu = cpu_baseline(inp, spec, min(n_cpu, B * H), alpha, delta, log)
 
     line = {
         "metric": "decode tokens/s at 1M ctx (1 GPU); achieved HBM GB/s vs peak",
@@ -328,7 +335,7 @@ def cpu_baseline(inp, spec, n_units, alpha, delta, log):
         O.decode_unit(qs, keys, vals, P, scale, alpha, "gauss", delta=delta)
         times.append(time.perf_counter() - t0)
     if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+        limiter.restore_original_limits()
     per_unit = statistics.mean(times)
     units_per_step = spec.batch * spec.num_kv_heads
     step_s = per_unit * units_per_step
