@@ -179,7 +179,11 @@ ekv_status ekv_select_topk(const ekv_paged_kv *kv, const float *ub, int32_t k,
  * largest margin max_h[(alpha-1) mhat_hp - tau_hat_h] is kept (lower index on
  * ties).  Outputs: sel/count as for top-k (ascending, count >= 1) and
  * tau_hat [batch][H_q] float32.  alpha must be 1.5 or 2 (r in {2, 1});
- * delta >= 0.  Workspace: ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0).
+ * delta >= 0.  Workspace: ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0)
+ * bytes (one 64-bit page mask per query head and 64-page tile), 256-byte
+ * aligned; its contents on entry do not matter.  tau_hat is found by
+ * Newton iterations in float32 that climb to the root from a proven lower
+ * bound (two kernels on the stream).
  */
 ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
                             float alpha, float delta, int32_t *sel,

@@ -153,8 +153,9 @@ size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
     case EKV_OP_SELECT_TOPK:  // candidate keys, whole tiles of pages
       return ((units * ekv::page_tiles(*kv) * ekv::kPageTile * 4) + 255) &
              ~static_cast<size_t>(255);
-    case EKV_OP_SELECT_GAUSS:
-      return 0;
+    case EKV_OP_SELECT_GAUSS:  // per (unit, query head) 64-bit page masks per tile
+      return ((units * kv->group * ekv::page_tiles(*kv) * 8) + 255) &
+             ~static_cast<size_t>(255);
     case EKV_OP_ENTMAX_DECODE:
       return ekv::decode_ws_layout(*kv).total;
     case EKV_OP_SOFTMAX_DECODE:
@@ -251,7 +252,7 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
   EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0)));
   const hipError_t e = with_g(*kv, [&](auto G) {
     return ekv::launch_select_gauss<decltype(G)::value>(
-        *kv, gstat, alpha, delta, sel, count, tau_hat, as_stream(stream));
+        *kv, gstat, alpha, delta, sel, count, tau_hat, ws, as_stream(stream));
   });
   return hip_status(e, "ekv_select_gauss launch");
 }

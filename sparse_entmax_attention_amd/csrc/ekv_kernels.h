@@ -60,7 +60,7 @@ hipError_t launch_select_topk(const ekv_paged_kv &kv, const float *ub, int k,
 template <int G>
 hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
                                float alpha, float delta, int32_t *sel,
-                               int32_t *count, float *tau_hat,
+                               int32_t *count, float *tau_hat, void *ws,
                                hipStream_t stream);
 template <class E, int D, int G>
 hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,

@@ -216,69 +216,340 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
 }
 
 // ---------------------------------------------------------------------------
-// Gaussian-aware selection, one block per unit.
+// Gaussian-aware selection.
 //
 // Threshold estimate per query head:
 //   m_p = (alpha-1) mu_p, s_p = (alpha-1) sigma_p, n_p valid tokens,
 //   F(tau) = sum_p n_p E[max(Z_p - tau, 0)^r],  Z_p ~ N(m_p, s_p^2).
 // F is decreasing and convex, and so is F^(1/r) (an L^r norm of a convex
-// non-negative function of tau).  Newton's method on F^(1/r) - 1 started at
-// tau_lo = max_p m_p - 1 (where F >= 1) therefore climbs monotonically to
-// the root without overshooting.  Pages with m_p + 8.5 s_p <= tau_lo add
-// less than ~1e-17 each for every tau >= tau_lo and are left out, first
-// tile by tile from the tile summaries, then page by page.
+// non-negative function of tau).  By Jensen, n E[(Z - tau)_+^r] >=
+// n (m - tau)_+^r, so F(m_p - n_p^(-1/r)) >= 1 for every page p: tau_lo =
+// max_p (m_p - n_p^(-1/r)) is a lower bound on the root, and Newton's method
+// on F^(1/r) - 1 started there climbs monotonically to the root without
+// overshooting.  (tau_lo is taken from the largest mean over the full pages
+// and over the last page, with their token counts.)  Pages with
+// m_p + 8.5 s_p <= tau_lo add less than ~1e-17 each for every tau >= tau_lo
+// and are left out ("survivors" are the others), first tile by tile from the
+// tile summaries, then page by page.
 //
 // Keep test: zhat = (alpha-1)(mu + sigma sqrt(2 ln n_p)) > tau_hat - delta
-// for some head; a tile is examined only if its summary
-// max(mu + sqrt(2 ln P) sigma) (an upper bound on every page's mu + sigma
-// sqrt(2 ln n_p), as n_p <= P) can pass for some head.
+// for some head.  Since tau_hat >= tau_lo, only tiles whose summary
+// max(mu + sqrt(2 ln P) sigma) clears tau_lo - delta can hold a kept page
+// (sqrt(2 ln n_p) <= sqrt(2 ln P)).
+//
+// Two kernels:
+//   k_gauss_tau, one block per (unit, query head): tau_lo from the tile
+//     summaries; ordered lists of the survivor tiles and of the keep
+//     candidate tiles; their pages loaded at once into LDS; Newton from LDS;
+//     tau_hat and, per tile, the 64-bit mask of the pages this head keeps
+//     (in the workspace).
+//   k_gauss_collect, one block per unit: the union of the heads' masks,
+//     written out in page order.
+// Lists or page data beyond the LDS capacities are read from global memory
+// instead (same arithmetic, slower).
 // ---------------------------------------------------------------------------
-constexpr int kSurvCap = 8192;    // survivor pages (all heads) in LDS
-constexpr int kTileListCap = 4096;
+constexpr int kGtThreads = 512;
+constexpr int kGtWaves = kGtThreads / kWave;
+constexpr int kGtSvItems = 128;   // survivor tiles whose (m, s) sit in LDS
+constexpr int kGtKzItems = 128;   // keep-candidate tiles whose zhat sit in LDS
+constexpr int kGtListCap = 4096;  // entries of each tile list
+constexpr float kPruneSigmas = 8.5f;
 
-struct GaussTerm {
-  double f, df;  // contribution to F and to -dF/dtau
-};
+// Standard normal tail pieces at c: Phi(c) and the density phi(c).
+// For a = |c|, the upper tail Q(a) = phi(a) R(a) with R the Mills ratio,
+// approximated by a degree 4 / degree 5 rational function with positive
+// coefficients, fitted for least maximum relative error on [0, 14] against
+// R(x) = sqrt(pi/2) erfcx(x / sqrt(2)): fit error 1.1e-8, about 4e-7 as
+// evaluated here in float32.  Its large-x behaviour is R ~ 1/x, as it should
+// be, and phi(a) underflows to 0 past a ~ 13.2.  Because Q is a product,
+// its relative accuracy holds far into the tail; Phi(c) = Q(-c) for c < 0
+// and 1 - Q(c) otherwise.
+__device__ __forceinline__ void norm_cdf_pdf(float c, float &Phi, float &phi) {
+  const float a = fabsf(c);
+  phi = 0.39894228040143268f *
+        __builtin_amdgcn_exp2f(-0.72134752044448170f * a * a);
+  float num = 9.571634593e-03f;
+  num = fmaf(num, a, 9.694951865e-02f);
+  num = fmaf(num, a, 4.449650583e-01f);
+  num = fmaf(num, a, 1.079636338e+00f);
+  num = fmaf(num, a, 1.253314139e+00f);
+  float den = 9.571468318e-03f;
+  den = fmaf(den, a, 9.695800140e-02f);
+  den = fmaf(den, a, 4.543498346e-01f);
+  den = fmaf(den, a, 1.178967137e+00f);
+  den = fmaf(den, a, 1.659309722e+00f);
+  den = fmaf(den, a, 1.0f);
+  const float q = phi * num * __builtin_amdgcn_rcpf(den);
+  Phi = c < 0.f ? q : 1.0f - q;
+}
 
-// n * E[(Z - tau)_+^r] and n * r * E[(Z - tau)_+^(r-1)] for Z ~ N(m, s^2).
-__device__ __forceinline__ GaussTerm gauss_term(float m, float s, float n,
-                                                float tau, int r) {
+// Adds n E[(Z - tau)_+^r] to f and n r E[(Z - tau)_+^(r-1)] to df for
+// Z ~ N(m, s^2) (closed forms: E[(Z-tau)_+] = u Phi + s phi and
+// E[(Z-tau)_+^2] = (u^2 + s^2) Phi + u s phi, u = m - tau, at c = u / s).
+__device__ __forceinline__ void gauss_term(float m, float s, float n, float tau,
+                                           int r, float &f, float &df) {
   const float u = m - tau;
   float Phi, phi;
   if (s > 0.f) {
-    const float c = u / s;
-    Phi = 0.5f * erfcf(-c * 0.70710678118654752f);
-    phi = 0.39894228040143268f * expf(-0.5f * c * c);
+    norm_cdf_pdf(u * __builtin_amdgcn_rcpf(s), Phi, phi);
   } else {
     Phi = u > 0.f ? 1.f : 0.f;
     phi = 0.f;
   }
-  const float e1 = u * Phi + s * phi;  // E[(Z - tau)_+]
-  GaussTerm t;
+  const float e1 = fmaf(u, Phi, s * phi);  // E[(Z - tau)_+]
   if (r == 2) {
-    const float e2 = (u * u + s * s) * Phi + u * s * phi;
-    t.f = static_cast<double>(n) * e2;
-    t.df = 2.0 * static_cast<double>(n) * e1;
+    const float e2 = fmaf(fmaf(u, u, s * s), Phi, u * s * phi);
+    f = fmaf(n, e2, f);
+    df = fmaf(2.0f * n, e1, df);
   } else {
-    t.f = static_cast<double>(n) * e1;
-    t.df = static_cast<double>(n) * Phi;
+    f = fmaf(n, e1, f);
+    df = fmaf(n, Phi, df);
   }
-  return t;
+}
+
+// Exclusive prefix sums of L counters over a block of NT threads (thread
+// order) and their totals.  smem holds L * NT / 64 ints.  Contains barriers.
+template <int NT, int L>
+__device__ __forceinline__ void block_scan_multi(const int (&x)[L], int (&pre)[L],
+                                                 int (&tot)[L], int *smem) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int incl[L];
+#pragma unroll
+  for (int l = 0; l < L; ++l) incl[l] = wave_incl_scan(x[l]);
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int l = 0; l < L; ++l) smem[l * NW + wid] = incl[l];
+  lds_barrier();
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    int base = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int v = smem[l * NW + w];
+      base += (w < wid) ? v : 0;
+      t += v;
+    }
+    pre[l] = base + incl[l] - x[l];
+    tot[l] = t;
+  }
 }
 
 template <int G>
-__global__ __launch_bounds__(kSelThreads) void k_select_gauss(
+__global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     const float *__restrict__ gstat, const int32_t *__restrict__ seq_lens,
     int batch, int H, int P, int max_pages, float am1, int r, float delta,
-    int32_t *__restrict__ sel, int32_t *__restrict__ count,
-    float *__restrict__ tau_hat) {
-  __shared__ float2 s_surv[kSurvCap];  // (m, s); s < 0 tags the last page
-  __shared__ int s_tiles[kTileListCap];
-  __shared__ int s_soff[G + 1];
-  __shared__ int s_cnt[kSelWaves];
-  __shared__ float s_red[kSelWaves][G];
-  __shared__ double s_fd[2][G][kSelWaves];
-  __shared__ float s_tau[G];
+    float *__restrict__ tau_hat, unsigned long long *__restrict__ masks) {
+  __shared__ float2 s_sv[kGtSvItems * kPageTile];  // (m, s); s < 0: last page
+  __shared__ float s_kz[kGtKzItems * kPageTile];
+  __shared__ int s_slist[kGtListCap];
+  __shared__ int s_klist[kGtListCap];
+  __shared__ int s_scan[2 * kGtWaves];
+  __shared__ float s_red[2][kGtWaves];
+  __shared__ float2 s_fd[2][kGtWaves];
+  const int u = blockIdx.x / G, g = blockIdx.x % G, b = u / H, h = u % H;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int len = seq_lens[b];
+  const int np = n_pages_of(len, P);
+  const int nt = (np + kPageTile - 1) / kPageTile;
+  const int Hq = H * G;
+  const int n_tiles = (max_pages + kPageTile - 1) / kPageTile;
+  const size_t row = static_cast<size_t>(b) * Hq + h * G + g;
+  const float2 *st = reinterpret_cast<const float2 *>(gstat) + row * max_pages;
+  const float4 *gt = reinterpret_cast<const float4 *>(
+                         gstat + gstat_tile_offset(batch, Hq, max_pages)) +
+                     row * n_tiles;
+  unsigned long long *mk = masks + (static_cast<size_t>(u) * G + g) * n_tiles;
+  const float last_n = static_cast<float>(page_tokens(np - 1, len, P));
+  const bool ragged = last_n < static_cast<float>(P);
+  const float full_c = sqrtf(2.0f * logf(static_cast<float>(P)));
+  const float last_c = sqrtf(2.0f * logf(last_n));
+
+  // 1. tau_lo.  Each thread owns a contiguous range of tiles and keeps the
+  // (.y, .z) summaries of its first one.  The last tile's summary may come
+  // from the partial last page, so that tile is read page by page.
+  const int per = (nt + kGtThreads - 1) / kGtThreads;
+  const int t_beg = min(nt, tid * per), t_end = min(nt, t_beg + per);
+  float2 c2 = make_float2(-FLT_MAX, -FLT_MAX);
+  float mx = -FLT_MAX, ml = -FLT_MAX;
+  for (int t = t_beg; t < t_end; ++t) {
+    const float4 v = gt[t];
+    if (t == t_beg) c2 = make_float2(v.y, v.z);
+    if (!(ragged && t == nt - 1)) mx = fmaxf(mx, v.x);
+  }
+  if (ragged && wave == 0) {
+    const int p = (nt - 1) * kPageTile + lane;
+    if (p < np) {
+      const float x = st[p].x;
+      if (p == np - 1) ml = x;
+      else mx = fmaxf(mx, x);
+    }
+  }
+  mx = group_max<kWave>(mx);
+  ml = group_max<kWave>(ml);
+  if (lane == 0) {
+    s_red[0][wave] = mx;
+    s_red[1][wave] = ml;
+  }
+  lds_barrier();
+  float M = s_red[0][0], ML = s_red[1][0];
+#pragma unroll
+  for (int w = 1; w < kGtWaves; ++w) {
+    M = fmaxf(M, s_red[0][w]);
+    ML = fmaxf(ML, s_red[1][w]);
+  }
+  const float inv_full = r == 2 ? rsqrtf(static_cast<float>(P))
+                                : 1.0f / static_cast<float>(P);
+  const float inv_last = r == 2 ? rsqrtf(last_n) : 1.0f / last_n;
+  const float tau_lo = fmaxf(am1 * M - inv_full, am1 * ML - inv_last);
+  // Tile tests get a small margin: they only prune, the page tests decide.
+  const float s_thr = tau_lo - 1e-5f * fmaxf(fabsf(tau_lo), 1.0f);
+  const float kc0 = tau_lo - delta;
+  const float k_thr = kc0 - 1e-5f * fmaxf(fabsf(kc0), 1.0f);
+
+  // 2. ordered lists of survivor tiles and keep-candidate tiles.
+  auto tile_flags = [&](int t, bool &sf, bool &kf) {
+    float2 v = c2;
+    if (t != t_beg) {
+      const float4 w = gt[t];
+      v = make_float2(w.y, w.z);
+    }
+    sf = am1 * v.x > s_thr;
+    kf = am1 * v.y > k_thr;
+  };
+  int cnt[2] = {0, 0}, pre[2], tot[2];
+  for (int t = t_beg; t < t_end; ++t) {
+    bool sf, kf;
+    tile_flags(t, sf, kf);
+    cnt[0] += sf;
+    cnt[1] += kf;
+  }
+  block_scan_multi<kGtThreads, 2>(cnt, pre, tot, s_scan);
+  const bool s_listed = tot[0] <= kGtListCap;
+  const bool k_listed = tot[1] <= kGtListCap;
+  const int n_st = s_listed ? tot[0] : nt;  // otherwise every tile, in order
+  const int n_kt = k_listed ? tot[1] : nt;
+  for (int t = t_beg; t < t_end; ++t) {
+    bool sf, kf;
+    tile_flags(t, sf, kf);
+    if (sf && s_listed) s_slist[pre[0]++] = t;
+    if (kf && k_listed) s_klist[pre[1]++] = t;
+    // Tiles that cannot hold a kept page get an empty mask here; the
+    // listed ones are written after the threshold is known.
+    if (!kf && k_listed) mk[t] = 0ull;
+  }
+  lds_barrier();
+  auto surv_tile = [&](int i) { return s_listed ? s_slist[i] : i; };
+  auto keep_tile = [&](int k) { return k_listed ? s_klist[k] : k; };
+  // (m, s) of page p, m = -inf if it is not a survivor, s < 0 (stored as
+  // -1 - s) tags the last page.
+  auto surv_entry = [&](int p) -> float2 {
+    if (p >= np) return make_float2(-INFINITY, 0.f);
+    const float2 v = st[p];
+    const float m = am1 * v.x, sd = am1 * sqrtf(fmaxf(v.y, 0.f));
+    if (!(m + kPruneSigmas * sd > tau_lo)) return make_float2(-INFINITY, 0.f);
+    return make_float2(m, p == np - 1 ? -1.0f - sd : sd);
+  };
+  auto zhat = [&](int p, const float2 v) {
+    const float c = (p == np - 1) ? last_c : full_c;
+    return am1 * (v.x + sqrtf(fmaxf(v.y, 0.f)) * c);
+  };
+
+  // 3. load the pages of both lists into LDS, loads of a round in flight
+  // together (entries wave, wave + 8, ...).
+  {
+    constexpr int KS = 4, KK = 4;
+    const int s_lim = min(n_st, kGtSvItems), k_lim = min(n_kt, kGtKzItems);
+    for (int c = 0;; ++c) {
+      const int si0 = wave + c * KS * kGtWaves;
+      const int ki0 = wave + c * KK * kGtWaves;
+      if (si0 >= s_lim && ki0 >= k_lim) break;
+      float2 kv[KK];
+      int kp[KK];
+#pragma unroll
+      for (int k = 0; k < KK; ++k) {
+        const int ki = ki0 + k * kGtWaves;
+        kp[k] = ki < k_lim ? keep_tile(ki) * kPageTile + lane : np;
+        kv[k] = kp[k] < np ? st[kp[k]] : make_float2(0.f, 0.f);
+      }
+      float2 sv[KS];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int si = si0 + k * kGtWaves;
+        sv[k] = si < s_lim ? surv_entry(surv_tile(si) * kPageTile + lane)
+                           : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int si = si0 + k * kGtWaves;
+        if (si < s_lim) s_sv[si * kPageTile + lane] = sv[k];
+      }
+#pragma unroll
+      for (int k = 0; k < KK; ++k) {
+        const int ki = ki0 + k * kGtWaves;
+        if (ki < k_lim)
+          s_kz[ki * kPageTile + lane] = kp[k] < np ? zhat(kp[k], kv[k]) : -INFINITY;
+      }
+    }
+  }
+  lds_barrier();
+
+  // 4. Newton on F^(1/r) - 1 from tau_lo; one wave reduction and one
+  // barrier per iteration (s_fd is double-buffered).
+  float tau = tau_lo;
+  for (int it = 0; it < 64; ++it) {
+    float f = 0.f, df = 0.f;
+    for (int i = wave; i < n_st; i += kGtWaves) {
+      const float2 e = i < kGtSvItems ? s_sv[i * kPageTile + lane]
+                                      : surv_entry(surv_tile(i) * kPageTile + lane);
+      if (e.x == -INFINITY) continue;
+      const bool last = e.y < 0.f;
+      gauss_term(e.x, last ? -1.0f - e.y : e.y,
+                 last ? last_n : static_cast<float>(P), tau, r, f, df);
+    }
+    f = group_sum<kWave>(f);
+    df = group_sum<kWave>(df);
+    if (lane == 0) s_fd[it & 1][wave] = make_float2(f, df);
+    lds_barrier();
+    float ff = 0.f, dd = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGtWaves; ++w) {
+      const float2 v = s_fd[it & 1][w];
+      ff += v.x;
+      dd += v.y;
+    }
+    // Every thread takes the same step from the same sums.
+    if (!(ff > 1.0f) || !(dd > 0.0f)) break;
+    const double F = ff;
+    const double step = (r == 2) ? 2.0 * (F - sqrt(F)) / dd : (F - 1.0) / dd;
+    const float next = static_cast<float>(static_cast<double>(tau) + step);
+    if (!(next > tau)) break;
+    tau = next;
+  }
+  if (tid == 0) tau_hat[row] = tau;
+
+  // 5. this head's keep masks of the candidate tiles.
+  const float cut = tau - delta;
+  for (int k = wave; k < n_kt; k += kGtWaves) {
+    const int t = keep_tile(k);
+    const int p = t * kPageTile + lane;
+    float z = -INFINITY;
+    if (k < kGtKzItems) z = s_kz[k * kPageTile + lane];
+    else if (p < np) z = zhat(p, st[p]);
+    const unsigned long long ball = __ballot(z > cut);
+    if (lane == 0) mk[t] = ball;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void k_gauss_collect(
+    const float *__restrict__ gstat, const int32_t *__restrict__ seq_lens,
+    int batch, int H, int P, int max_pages, float am1,
+    const unsigned long long *__restrict__ masks,
+    const float *__restrict__ tau_hat, int32_t *__restrict__ sel,
+    int32_t *__restrict__ count) {
+  __shared__ unsigned long long s_mask[kSelThreads];
+  __shared__ int s_off[kSelThreads];
   __shared__ int tmp[kSelWaves];
   __shared__ float s_gap[kSelWaves];
   __shared__ int s_idx[kSelWaves];
@@ -287,195 +558,34 @@ __global__ __launch_bounds__(kSelThreads) void k_select_gauss(
   const int len = seq_lens[b];
   const int np = n_pages_of(len, P);
   const int nt = (np + kPageTile - 1) / kPageTile;
-  const int Hq = H * G;
   const int n_tiles = (max_pages + kPageTile - 1) / kPageTile;
-  const float2 *st = reinterpret_cast<const float2 *>(gstat) +
-                     (static_cast<size_t>(b) * Hq + h * G) * max_pages;
-  const float4 *gt = reinterpret_cast<const float4 *>(
-                         gstat + gstat_tile_offset(batch, Hq, max_pages)) +
-                     (static_cast<size_t>(b) * Hq + h * G) * n_tiles;
-  const float last_n = static_cast<float>(page_tokens(np - 1, len, P));
+  const unsigned long long *mk = masks + static_cast<size_t>(u) * G * n_tiles;
   const unsigned long long below = (1ull << lane) - 1ull;
-
-  // 1. largest page mean per head, from the tile summaries
-  float mx[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -FLT_MAX;
-  for (int t = tid; t < nt; t += kSelThreads)
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      mx[g] = fmaxf(mx[g], gt[static_cast<size_t>(g) * n_tiles + t].x);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float m = group_max<kWave>(mx[g]);
-    if (lane == 0) s_red[wave][g] = m;
-  }
-  lds_barrier();
-  float tau_lo[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = s_red[0][g];
-    for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, s_red[w][g]);
-    tau_lo[g] = am1 * m - 1.0f;
-  }
-
-  // 2. survivors of every head, in (head, page) order, in LDS: tiles whose
-  // summary passes, then one tile per wave and an ordered write per round.
-  bool surv_ok = true;
-  int n_surv = 0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (tid == 0) s_soff[g] = n_surv;
-    const float tl = tau_lo[g];
-    const int n_st = ordered_list(
-        nt, [&](int t) { return am1 * gt[static_cast<size_t>(g) * n_tiles + t].y > tl; },
-        s_tiles, kTileListCap, tmp);
-    if (n_st > kTileListCap) surv_ok = false;
-    const int n_use = surv_ok ? n_st : 0;
-    for (int r0 = 0; r0 < n_use; r0 += kSelWaves) {
-      const int ti = r0 + wave;
-      const int p = ti < n_use ? s_tiles[ti] * kPageTile + lane : np;
-      float m = 0.f, sd = 0.f;
-      bool ok = false;
-      if (p < np) {
-        const float2 v = st[static_cast<size_t>(g) * max_pages + p];
-        m = am1 * v.x;
-        sd = am1 * sqrtf(fmaxf(v.y, 0.f));
-        ok = m + 8.5f * sd > tl;
-      }
-      const unsigned long long ball = __ballot(ok);
-      if (lane == 0) s_cnt[wave] = __popcll(ball);
-      lds_barrier();
-      int off = n_surv, tot = 0;
-      for (int w = 0; w < kSelWaves; ++w) {
-        off += (w < wave) ? s_cnt[w] : 0;
-        tot += s_cnt[w];
-      }
-      const int pos = off + __popcll(ball & below);
-      if (ok && pos < kSurvCap)
-        s_surv[pos] = make_float2(m, p == np - 1 ? -1.0f - sd : sd);
-      n_surv += tot;
-      lds_barrier();
-    }
-    if (n_surv > kSurvCap) surv_ok = false;
-  }
-  if (tid == 0) s_soff[G] = n_surv;
-  lds_barrier();
-
-  // 3. Newton for all heads together, one block reduction per iteration.
-  float tau[G];
-  bool done[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) { tau[g] = tau_lo[g]; done[g] = false; }
-  for (int it = 0; it < 64; ++it) {
-    double f[G], df[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      f[g] = 0.0;
-      df[g] = 0.0;
-      if (done[g]) continue;
-      if (surv_ok) {
-        for (int i = s_soff[g] + tid; i < s_soff[g + 1]; i += kSelThreads) {
-          const float2 e = s_surv[i];
-          const bool last = e.y < 0.f;
-          const GaussTerm t = gauss_term(e.x, last ? -1.0f - e.y : e.y,
-                                         last ? last_n : static_cast<float>(P),
-                                         tau[g], r);
-          f[g] += t.f;
-          df[g] += t.df;
-        }
-      } else {
-        for (int p = tid; p < np; p += kSelThreads) {
-          const float2 v = st[static_cast<size_t>(g) * max_pages + p];
-          const float m = am1 * v.x, sd = am1 * sqrtf(fmaxf(v.y, 0.f));
-          if (m + 8.5f * sd > tau_lo[g]) {
-            const GaussTerm t = gauss_term(
-                m, sd, p == np - 1 ? last_n : static_cast<float>(P), tau[g], r);
-            f[g] += t.f;
-            df[g] += t.df;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      f[g] = group_sum_d<kWave>(f[g]);
-      df[g] = group_sum_d<kWave>(df[g]);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) { s_fd[0][g][wave] = f[g]; s_fd[1][g][wave] = df[g]; }
-    }
-    lds_barrier();
-    bool all_done = true;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (done[g]) continue;
-      double ff = 0.0, dd = 0.0;
-      for (int w = 0; w < kSelWaves; ++w) { ff += s_fd[0][g][w]; dd += s_fd[1][g][w]; }
-      if (!(ff > 1.0) || !(dd > 0.0)) { done[g] = true; continue; }
-      const double step = (r == 2) ? 2.0 * (ff - sqrt(ff)) / dd : (ff - 1.0) / dd;
-      const float next = static_cast<float>(static_cast<double>(tau[g]) + step);
-      if (!(next > tau[g])) { done[g] = true; continue; }
-      tau[g] = next;
-      all_done = false;
-    }
-    lds_barrier();  // s_fd is rewritten by the next iteration
-    if (all_done) break;
-  }
-  if (tid < G) {
-    float tg = tau[0];
-#pragma unroll
-    for (int g = 1; g < G; ++g) if (g == tid) tg = tau[g];
-    s_tau[tid] = tg;
-    tau_hat[b * Hq + h * G + tid] = tg;
-  }
-  lds_barrier();
-
-  // 4. keep test over the tiles that can pass, ordered write per round.
-  float cut[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) cut[g] = s_tau[g] - delta;
-  const float full_c = sqrtf(2.0f * logf(static_cast<float>(P)));
-  const float last_c = sqrtf(2.0f * logf(last_n));
-  const int n_kt = ordered_list(
-      nt,
-      [&](int t) {
-        bool any = false;
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          any |= am1 * gt[static_cast<size_t>(g) * n_tiles + t].z > cut[g];
-        return any;
-      },
-      s_tiles, kTileListCap, tmp);
-  const bool kt_listed = n_kt <= kTileListCap;
-  const int n_scan = kt_listed ? n_kt : nt;
   int32_t *out = sel + static_cast<size_t>(u) * max_pages;
+
+  // Chunks of kSelThreads tiles: union of the heads' masks, exclusive scan
+  // of the page counts, then one wave per tile writes its pages in order.
   int total = 0;
-  for (int r0 = 0; r0 < n_scan; r0 += kSelWaves) {
-    const int ti = r0 + wave;
-    const int tile = ti < n_scan ? (kt_listed ? s_tiles[ti] : ti) : nt;
-    const int p = tile * kPageTile + lane;
-    bool keep = false;
-    if (p < np) {
-      const float c = (p == np - 1) ? last_c : full_c;
+  for (int c0 = 0; c0 < nt; c0 += kSelThreads) {
+    const int t = c0 + tid;
+    unsigned long long m = 0ull;
+    if (t < nt) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float2 v = st[static_cast<size_t>(g) * max_pages + p];
-        keep |= am1 * (v.x + sqrtf(fmaxf(v.y, 0.f)) * c) > cut[g];
-      }
+      for (int g = 0; g < G; ++g) m |= mk[static_cast<size_t>(g) * n_tiles + t];
     }
-    const unsigned long long ball = __ballot(keep);
-    if (lane == 0) s_cnt[wave] = __popcll(ball);
+    int ctot;
+    const int pre = block_excl_scan<kSelThreads>(__popcll(m), tmp, ctot);
+    s_mask[tid] = m;
+    s_off[tid] = total + pre;
     lds_barrier();
-    int off = total, tot = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      off += (w < wave) ? s_cnt[w] : 0;
-      tot += s_cnt[w];
+    const int n_c = min(kSelThreads, nt - c0);
+    for (int j = wave; j < n_c; j += kSelWaves) {
+      const unsigned long long mm = s_mask[j];
+      if ((mm >> lane) & 1ull)
+        out[s_off[j] + __popcll(mm & below)] = (c0 + j) * kPageTile + lane;
     }
-    if (keep) out[off + __popcll(ball & below)] = p;
-    total += tot;
-    lds_barrier();
+    total += ctot;
+    lds_barrier();  // s_mask and s_off are rewritten by the next chunk
   }
   if (total > 0) {
     if (tid == 0) count[u] = total;
@@ -483,6 +593,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_gauss(
   }
   // Nothing kept: the page with the largest margin
   // max_g (zhat_g - tau_hat_g), lower index on ties (all pages scanned).
+  const int Hq = H * G;
+  const float2 *st = reinterpret_cast<const float2 *>(gstat) +
+                     (static_cast<size_t>(b) * Hq + h * G) * max_pages;
+  const float *th = tau_hat + static_cast<size_t>(b) * Hq + h * G;
+  const float last_n = static_cast<float>(page_tokens(np - 1, len, P));
+  const float full_c = sqrtf(2.0f * logf(static_cast<float>(P)));
+  const float last_c = sqrtf(2.0f * logf(last_n));
   float best = -FLT_MAX;
   int bi = np;
   for (int p = tid; p < np; p += kSelThreads) {
@@ -491,7 +608,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_gauss(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float2 v = st[static_cast<size_t>(g) * max_pages + p];
-      mg = fmaxf(mg, am1 * (v.x + sqrtf(fmaxf(v.y, 0.f)) * c) - s_tau[g]);
+      mg = fmaxf(mg, am1 * (v.x + sqrtf(fmaxf(v.y, 0.f)) * c) - th[g]);
     }
     if (mg > best) { best = mg; bi = p; }
   }
@@ -532,13 +649,21 @@ hipError_t launch_select_topk(const ekv_paged_kv &kv, const float *ub, int k,
 template <int G>
 hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
                                float alpha, float delta, int32_t *sel,
-                               int32_t *count, float *tau_hat,
+                               int32_t *count, float *tau_hat, void *ws,
                                hipStream_t stream) {
   const int r = alpha == 2.0f ? 1 : 2;
-  hipLaunchKernelGGL((k_select_gauss<G>), dim3(kv.batch * kv.num_kv_heads),
-                     dim3(kSelThreads), 0, stream, gstat, kv.seq_lens,
-                     kv.batch, kv.num_kv_heads, kv.page_size, kv.max_pages,
-                     alpha - 1.0f, r, delta, sel, count, tau_hat);
+  const int units = kv.batch * kv.num_kv_heads;
+  auto *masks = static_cast<unsigned long long *>(ws);
+  hipLaunchKernelGGL((k_gauss_tau<G>), dim3(units * G), dim3(kGtThreads), 0,
+                     stream, gstat, kv.seq_lens, kv.batch, kv.num_kv_heads,
+                     kv.page_size, kv.max_pages, alpha - 1.0f, r, delta,
+                     tau_hat, masks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gauss_collect<G>), dim3(units), dim3(kSelThreads), 0,
+                     stream, gstat, kv.seq_lens, kv.batch, kv.num_kv_heads,
+                     kv.page_size, kv.max_pages, alpha - 1.0f, masks, tau_hat,
+                     sel, count);
   return hipGetLastError();
 }
 
@@ -548,7 +673,7 @@ hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
                                             int32_t *, void *, hipStream_t); \
   template hipError_t launch_select_gauss<G>(                                \
       const ekv_paged_kv &, const float *, float, float, int32_t *,          \
-      int32_t *, float *, hipStream_t);
+      int32_t *, float *, void *, hipStream_t);
 EKV_FOR_EACH_G(EKV_INST_SEL)
 
 }  // namespace ekv

@@ -65,6 +65,8 @@ def test_workspace_sizes(lib):
     assert dec % 256 == 0
     topk = lib.ekv_workspace_size(B.EKV_OP_SELECT_TOPK, ctypes.byref(kv), 16)
     assert topk >= units * 1024 * 4
+    gauss = lib.ekv_workspace_size(B.EKV_OP_SELECT_GAUSS, ctypes.byref(kv), 0)
+    assert gauss == units * G * ((1024 + 63) // 64) * 8  # page mask per head and tile
     assert lib.ekv_workspace_size(99, ctypes.byref(kv), 0) == 0
     # score buffers: per-page values plus 64-page tile summaries
     T = (1024 + 63) // 64
