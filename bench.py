@@ -12,7 +12,10 @@ full-cache entmax and split-K softmax baselines are timed the same way.
 
 Each kernel of a step is bracketed by HIP events on the stream the library
 launches on (torch's current stream), which gives the per-kernel durations
-used for the roofline of the dominant kernel.
+used for the roofline of the dominant kernel.  The events are created with
+a device-scope release (hipEventReleaseToDevice): the default system-scope
+release flushes the caches at every record and would add several
+microseconds between the kernels of a step.
 
 Prints ONE JSON line.
 """
@@ -30,6 +33,59 @@ REPO = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, REPO)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+# hipEventReleaseToDevice: the event is recorded with a device-scope
+# release.  The default (system-scope) release writes back and invalidates
+# the caches at every record, which adds several microseconds between
+# kernels and would be charged to the decode step.
+HIP_EVENT_RELEASE_TO_DEVICE = 0x40000000
+
+
+class DeviceEvents:
+    """Timing events on the HIP runtime that torch already loaded."""
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), HIP_EVENT_RELEASE_TO_DEVICE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+        self.pool.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return out.value
+
+    def close(self):
+        for e in self.pool:
+            self.lib.hipEventDestroy(e)
+        self.pool = []
 
 
 def parse():
@@ -95,13 +151,15 @@ def main():
     # 2 GiB (well beyond the 256 MB last-level cache), median of 5.
     probe = torch.ones(512 << 20, dtype=torch.float32, device=dev)
     sink = torch.empty(ekv.EKV_READ_PROBE_SINK, dtype=torch.int32, device=dev)
-    pe = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
+    dev_ev = DeviceEvents()
+    pe = [dev_ev.new() for _ in range(12)]
     for i in range(6):
-        pe[2 * i].record(stream)
+        dev_ev.record(pe[2 * i], stream)
         ekv.ekv_read_probe(probe, sink)
-        pe[2 * i + 1].record(stream)
+        dev_ev.record(pe[2 * i + 1], stream)
     torch.cuda.synchronize()
-    probe_ms = statistics.median(pe[2 * i].elapsed_time(pe[2 * i + 1]) for i in range(1, 6))
+    probe_ms = statistics.median(dev_ev.ms(pe[2 * i], pe[2 * i + 1]) for i in range(1, 6))
+    dev_ev.close()
     read_probe_gbps = probe.numel() * 4 / (probe_ms * 1e-3) / 1e9
     del probe, sink
     # A write of known size (256 MiB), the reference for hardware write counters.
@@ -111,12 +169,13 @@ def main():
     del calib
 
     # Full metadata build (once; timed on its own).
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    ev0, ev1 = dev_ev.new(), dev_ev.new()
+    dev_ev.record(ev0, stream)
     buf.build_meta()
-    ev1.record(stream)
+    dev_ev.record(ev1, stream)
     torch.cuda.synchronize()
-    meta_build_ms = ev0.elapsed_time(ev1)
+    meta_build_ms = dev_ev.ms(ev0, ev1)
+    dev_ev.close()
 
     # Each leg is a list of (phase name, callable).
     def ph_meta():
@@ -159,31 +218,50 @@ def main():
     }
 
     def run_leg(name, steps, warmup):
+        """Headline pass: one event pair per step (start, end).  Breakdown
+        pass: the same steps with an event after every kernel, for the
+        per-kernel durations (each event between kernels adds a few
+        microseconds of dispatch delay, so it is kept out of the headline)."""
         phases = legs[name]
         for _ in range(warmup):
             for _, fn in phases:
                 fn()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-               for _ in range(steps)]
+
+        evs = [(dev_ev.new(), dev_ev.new()) for _ in range(steps)]
         t_start = time.perf_counter()
         for s in range(steps):
             if flush is not None:
                 flush(s)
-            evs[s][0].record(stream)
-            for i, (_, fn) in enumerate(phases):
+            dev_ev.record(evs[s][0], stream)
+            for _, fn in phases:
                 fn()
-                evs[s][i + 1].record(stream)
+            dev_ev.record(evs[s][1], stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t_start) / steps
-        step_ms = [evs[s][0].elapsed_time(evs[s][-1]) for s in range(steps)]
-        phase_ms = {pname: statistics.mean(evs[s][i].elapsed_time(evs[s][i + 1])
+        step_ms = [dev_ev.ms(a, b) for a, b in evs]
+        dev_ev.close()
+
+        pev = [[dev_ev.new() for _ in range(len(phases) + 1)] for _ in range(steps)]
+        for s in range(steps):
+            if flush is not None:
+                flush(s)
+            dev_ev.record(pev[s][0], stream)
+            for i, (_, fn) in enumerate(phases):
+                fn()
+                dev_ev.record(pev[s][i + 1], stream)
+        torch.cuda.synchronize()
+        phase_ms = {pname: statistics.mean(dev_ev.ms(pev[s][i], pev[s][i + 1])
                                            for s in range(steps))
                     for i, (pname, _) in enumerate(phases)}
+        phased_step_ms = statistics.median(dev_ev.ms(pev[s][0], pev[s][-1])
+                                           for s in range(steps))
+        dev_ev.close()
         return {"median_ms": statistics.median(step_ms),
                 "p10_ms": float(np.percentile(step_ms, 10)),
                 "p90_ms": float(np.percentile(step_ms, 90)),
-                "wall_ms_incl_flush": wall * 1e3, "phase_ms": phase_ms}
+                "wall_ms_incl_flush": wall * 1e3, "phase_ms": phase_ms,
+                "median_ms_with_phase_events": phased_step_ms}
 
     def selection_stats():
         cnt = buf.count.cpu().numpy()

@@ -280,12 +280,13 @@ ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
                                 const int32_t *sel, const int32_t *count,
                                 float *tau, void *ws, size_t ws_bytes,
                                 void *stream) {
-  EKV_TRY(check_kv(kv, false, false));
+  EKV_TRY(check_kv(kv, false, true));
   EKV_TRY(check_alpha(alpha));
   EKV_TRY(check_sel(sel, count));
   EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0)));
-  const hipError_t e = with_g(*kv, [&](auto G) {
-    return ekv::launch_entmax_threshold<decltype(G)::value>(
+  const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
+    return ekv::launch_entmax_threshold<decltype(E), decltype(D)::value,
+                                        decltype(G)::value>(
         *kv, alpha, sel, count, tau, ws, as_stream(stream));
   });
   return hip_status(e, "ekv_entmax_threshold launch");

@@ -42,7 +42,11 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   w.tau = al(w.cmax + units * G * static_cast<size_t>(kv.max_pages) * 4);
   w.part_o = al(w.tau + units * G * 4);
   w.part_s = al(w.part_o + units * mc * G * D * 4);
-  w.total = al(w.part_s + units * mc * G * 4);
+  w.head_o = al(w.part_s + units * mc * G * 4);
+  w.head_s = al(w.head_o + units * G * D * 4);
+  w.done = al(w.head_s + units * G * 4);
+  w.slot = al(w.done + units * G * 4);  // pool slot per selected page
+  w.total = al(w.slot + units * static_cast<size_t>(kv.max_pages) * 4);
   return w;
 }
 
@@ -71,22 +75,31 @@ __device__ __forceinline__ int unit_pages(const int32_t *seq_lens,
 }
 
 // pref[u] = first item of unit u (pref[units] = total); returns the total.
+// With `done` (one flag per query head, G per unit), units whose heads are
+// all done contribute no items.
 template <int NT>
 __device__ int build_unit_prefix(int *pref, int *tmp, const int32_t *seq_lens,
                                  const int32_t *sel, const int32_t *count,
-                                 int units, int H, int P, int pages_per_item) {
+                                 int units, int H, int P, int pages_per_item,
+                                 const int32_t *done = nullptr, int G = 0) {
   const int per = (units + NT - 1) / NT;
   const int u0 = threadIdx.x * per, u1 = min(units, u0 + per);
+  auto items = [&](int u) {
+    if (done) {
+      bool all = true;
+      for (int g = 0; g < G; ++g) all &= done[u * G + g] != 0;
+      if (all) return 0;
+    }
+    return (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
+           pages_per_item;
+  };
   int local = 0;
-  for (int u = u0; u < u1; ++u)
-    local += (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
-             pages_per_item;
+  for (int u = u0; u < u1; ++u) local += items(u);
   int total;
   int base = block_excl_scan<NT>(local, tmp, total);
   for (int u = u0; u < u1; ++u) {
     pref[u] = base;
-    base += (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
-            pages_per_item;
+    base += items(u);
   }
   if (threadIdx.x == 0) pref[units] = total;
   lds_barrier();
@@ -183,7 +196,8 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
     float zscale, int units, int H, int max_pages, int cap,
-    float *__restrict__ zbuf, float *__restrict__ pmax) {
+    float *__restrict__ zbuf, float *__restrict__ pmax,
+    int32_t *__restrict__ slots) {
   constexpr int KS = D / 32;            // k-steps of 32 coordinates
   constexpr int NPASS = (G + 3) / 4;    // groups of 4 query heads
   constexpr int NT16 = P / 16;          // 16-token groups per page
@@ -261,6 +275,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
             pmax[(static_cast<size_t>(u) * G + g) * max_pages + cur.j] = m;
         }
       }
+    if (lane == 0) slots[static_cast<size_t>(u) * max_pages + cur.j] = cur.slot;
     if (fn >= total) break;
     f = fn;
     cur = nxt;
@@ -278,7 +293,8 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
     float zscale, int units, int H, int P, int max_pages, int cap,
-    float *__restrict__ zbuf, float *__restrict__ pmax) {
+    float *__restrict__ zbuf, float *__restrict__ pmax,
+    int32_t *__restrict__ slots) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   __shared__ int pref[kMaxUnits + 1];
@@ -324,6 +340,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
       const float m = group_max<kWave>(mx[g]);
       if (lane == 0) pmax[(static_cast<size_t>(u) * G + g) * max_pages + r.j] = m;
     }
+    if (lane == 0) slots[static_cast<size_t>(u) * max_pages + r.j] = r.slot;
   }
 }
 
@@ -353,23 +370,30 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
 // the order the block visits the tokens.  General alpha, or a bracket with
 // too many undecided tokens, falls back to bisection in double.
 // ---------------------------------------------------------------------------
-constexpr int kTauThreads = 1024;
+constexpr int kTauThreads = 512;
 constexpr int kTauBins = 2048;
 constexpr int kTauList = 1024;
-constexpr int kTauPageCap = 8192;
-constexpr int kTauCandCap = 16384;
-constexpr int kTauMaxBins = 1024;
+constexpr int kTauPageCap = 4096;
+constexpr int kTauCandCap = 8192;
+constexpr int kTauMaxBins = 512;
+constexpr int kTauIters = 64;  // support iterations before the fallback
 constexpr double kFix = 1099511627776.0;  // 2^40
 
 __device__ __forceinline__ long long fixp(double x) {
   return static_cast<long long>(rint(x * kFix));
 }
 
+template <int W>
+__device__ __forceinline__ long long group_sum_ll(long long x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
 template <int NT>
 __device__ __forceinline__ long long block_sum_ll(long long x, long long *smem) {
   constexpr int NW = NT / kWave;
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  x = group_sum_ll<kWave>(x);
   lds_barrier();
   if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = x;
   lds_barrier();
@@ -429,72 +453,81 @@ __device__ __forceinline__ double block_incl_scan_d(double x, double *smem) {
   return base + x;
 }
 
+template <class E, int D>
 __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     const float *__restrict__ zbuf, const float *__restrict__ pmax,
+    const typename E::T *__restrict__ vpool,
+    const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, int H, int G, int P, int max_pages,
     int cap, int r, float rg, float *__restrict__ tau_ws,
-    float *__restrict__ tau_user) {
+    float *__restrict__ tau_user, float *__restrict__ head_o,
+    float *__restrict__ head_s, int32_t *__restrict__ done,
+    const int32_t *__restrict__ slots) {
   constexpr int NW = kTauThreads / kWave;
   constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
+  constexpr int CSEG = kTauCandCap / NW;  // staged candidates per wave
   __shared__ unsigned int hist[kTauBins];
   __shared__ int cpages[NW][SEGP];
-  __shared__ float cand[kTauCandCap];
+  __shared__ float cand[kTauCandCap];   // z of the staged candidates
+  __shared__ int cpos[kTauCandCap];     // their positions jj * P + t
+  __shared__ float s_vacc[NW][D];
+  __shared__ float s_vsum[NW];
   __shared__ float list[kTauList];
-  __shared__ int s_ncand, s_nlist;
+  __shared__ int s_nlist;
   __shared__ int s_npg[NW];
-  __shared__ int s_seg[NW + 1];
+  __shared__ int dense[kTauPageCap];   // listed pages (selection index j)
+  __shared__ int dslot[kTauPageCap];   // their pool slots
   __shared__ float red_f[NW];
   __shared__ int red_i[NW];
   __shared__ double red_d[NW];
   __shared__ long long red_ll[NW];
   __shared__ double s_best_t;
   __shared__ double s_tot[3];
+  __shared__ int s_ccnt[NW];
+  __shared__ int s_wsolved;
+  __shared__ double s_wtau;
 
   const int ug = blockIdx.x, u = ug / G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   const float *zh = zbuf + static_cast<size_t>(ug) * cap;
   const float *pm = pmax + static_cast<size_t>(ug) * max_pages;
-  constexpr int U = 8;
+  constexpr int U = 32;
 
+  // Page maxima, read once: thread (wave, lane) holds pages
+  // tid + k * kTauThreads, k < U (one 64-page tile per wave and k); pages
+  // beyond U * kTauThreads (very long selections) are re-read when needed.
+  static_assert(kTauMaxBins <= kTauBins, "page-maximum bins reuse hist");
+  constexpr int CACHED = kTauThreads * U;
+  float pv[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int j = tid + k * kTauThreads;
+    pv[k] = j < cnt ? pm[j] : -FLT_MAX;
+  }
+  for (int i = tid; i < kTauMaxBins; i += kTauThreads) hist[i] = 0u;
   // Largest score.
   float mloc = -FLT_MAX;
-  for (int j0 = tid; j0 < cnt; j0 += kTauThreads * U) {
-    float v[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int j = j0 + k * kTauThreads;
-      v[k] = j < cnt ? pm[j] : -FLT_MAX;
-    }
-#pragma unroll
-    for (int k = 0; k < U; ++k) mloc = fmaxf(mloc, v[k]);
-  }
-  const float M = block_max<kTauThreads>(mloc, red_f);
+  for (int k = 0; k < U; ++k) mloc = fmaxf(mloc, pv[k]);
+  for (int j = CACHED + tid; j < cnt; j += kTauThreads) mloc = fmaxf(mloc, pm[j]);
+  const float M = block_max<kTauThreads>(mloc, red_f);  // also orders hist
   const double Md = M;
 
   // Tighter lower bracket from the page maxima within 1 of M: with C_b the
   // number of page maxima in bins >= b (all at least the bin's lower edge
   // e_b), tau >= e_b - C_b^(-1/r).
-  static_assert(kTauMaxBins <= kTauBins, "page-maximum bins reuse hist");
-  for (int i = tid; i < kTauMaxBins; i += kTauThreads) hist[i] = 0u;
-  lds_barrier();
-  for (int j0 = tid; j0 < cnt; j0 += kTauThreads * U) {
-    float v[U];
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int j = j0 + k * kTauThreads;
-      v[k] = j < cnt ? pm[j] : -FLT_MAX;
+  auto count_max = [&](float v) {
+    const double x = (static_cast<double>(v) - (Md - 1.0)) * kTauMaxBins;
+    if (x > 0.0) {
+      const int bn = x < kTauMaxBins ? static_cast<int>(x) : kTauMaxBins - 1;
+      atomicAdd(&hist[bn], 1u);
     }
+  };
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const double x = (static_cast<double>(v[k]) - (Md - 1.0)) * kTauMaxBins;
-      if (x > 0.0) {
-        const int bn = x < kTauMaxBins ? static_cast<int>(x) : kTauMaxBins - 1;
-        atomicAdd(&hist[bn], 1u);
-      }
-    }
-  }
+  for (int k = 0; k < U; ++k) count_max(pv[k]);
+  for (int j = CACHED + tid; j < cnt; j += kTauThreads) count_max(pm[j]);
   lds_barrier();
   double Lloc = Md - 1.0;
   {
@@ -515,81 +548,95 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   // Snap down to a multiple of 2^-24 so that z - L is exact in double.
   L = floor(L * 16777216.0) / 16777216.0;
 
-  // Pages whose maximum exceeds L: each wave lists, in page order, those of
-  // its interleaved 64-page tiles (no block barrier; loads batched).
+  // Pages whose maximum exceeds L: each wave lists those of its 64-page
+  // tiles (in page order within the wave), then the lists are laid end to
+  // end in `dense`.
   int npw = 0;
-  for (int t0 = wave * kWave; t0 < cnt; t0 += kTauThreads * 2) {
-    float v[2];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  auto list_page = [&](int j, float v) {  // called by whole waves
+    const bool flag = j < cnt && static_cast<double>(v) > L;
+    const unsigned long long ball = __ballot(flag);
+    const int rk = npw + __popcll(ball & below);
+    if (flag && rk < SEGP) cpages[wave][rk] = j;
+    npw += __popcll(ball);
+  };
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = t0 + k * kTauThreads + lane;
-      v[k] = j < cnt ? pm[j] : -FLT_MAX;
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int j = t0 + k * kTauThreads + lane;
-      const bool flag = j < cnt && static_cast<double>(v[k]) > L;
-      const unsigned long long ball = __ballot(flag);
-      const int rk = npw + __popcll(ball & ((1ull << lane) - 1ull));
-      if (flag && rk < SEGP) cpages[wave][rk] = j;
-      npw += __popcll(ball);
-    }
+  for (int k = 0; k < U; ++k) list_page(tid + k * kTauThreads, pv[k]);
+  for (int jb = CACHED + wave * kWave; jb < cnt; jb += kTauThreads) {
+    const int j = jb + lane;
+    list_page(j, j < cnt ? pm[j] : -FLT_MAX);
   }
   if (lane == 0) s_npg[wave] = npw;
-  if (tid == 0) { s_ncand = 0; s_nlist = 0; }
+  if (tid == 0) s_nlist = 0;
   lds_barrier();
   bool listed = true;
-  int n_listed = 0;
+  int n_listed = 0, seg0 = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    listed &= s_npg[w] <= SEGP;
-    n_listed += s_npg[w];
+    const int c = s_npg[w];
+    listed &= c <= SEGP;
+    seg0 += (w < wave) ? c : 0;
+    n_listed += c;
   }
-  if (tid == 0) {
-    int acc = 0;
-    for (int w = 0; w < NW; ++w) { s_seg[w] = acc; acc += s_npg[w]; }
-    s_seg[NW] = acc;
-  }
+  if (listed)
+    for (int i = lane; i < npw; i += kWave) dense[seg0 + i] = cpages[wave][i];
   lds_barrier();
   const int n_pg = listed ? n_listed : cnt;
-  auto page_of = [&](int jj) {  // jj-th listed page (or jj itself)
-    if (!listed) return jj;
-    int w = 0;
-    for (int k = 1; k < NW; ++k) w += jj >= s_seg[k];
-    return cpages[w][jj - s_seg[w]];
-  };
+  auto page_of = [&](int jj) { return listed ? dense[jj] : jj; };
 
-  // Stage the candidates z > L in LDS (order irrelevant downstream).
+  // Stage the candidates z > L in LDS, wave w appending to its own segment
+  // cand[w * CSEG ..] in a fixed order (no atomics, so the order does not
+  // change from run to run).  A wave step covers kWave / P listed pages, one
+  // token per lane, with US steps in flight.
   {
-    const int span = n_pg * P;
-    for (int base = 0; base < span; base += kTauThreads * U) {
-      float zv[U];
+    constexpr int US = 32;
+    const int ppw = kWave / P, sub = lane / P, t = lane - sub * P;
+    const int steps = (n_pg + ppw - 1) / ppw;
+    int nc = 0;
+    for (int s0 = wave; s0 < steps; s0 += NW * US) {
+      float zv[US];
+      int zp[US], zs[US];
 #pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int fi = base + k * kTauThreads + tid;
+      for (int k = 0; k < US; ++k) {
+        const int jj = (s0 + k * NW) * ppw + sub;
         zv[k] = -INFINITY;
-        if (fi < span) {
-          const int jj = fi / P, t = fi - jj * P;
+        zp[k] = 0;
+        zs[k] = 0;
+        if (jj < n_pg) {
           const int j = page_of(jj);
+          zp[k] = jj * P + t;
           if (listed || static_cast<double>(pm[j]) > L)
             zv[k] = zh[static_cast<size_t>(j) * P + t];
+          // the page's pool slot (written by the score pass), for the
+          // value gather at the end; loaded alongside the scores
+          if (listed && t == 0) zs[k] = slots[static_cast<size_t>(u) * max_pages + j];
         }
       }
 #pragma unroll
-      for (int k = 0; k < U; ++k)
-        if (static_cast<double>(zv[k]) > L) {
-          const int sidx = atomicAdd(&s_ncand, 1);
-          if (sidx < kTauCandCap) cand[sidx] = zv[k];
+      for (int k = 0; k < US; ++k) {
+        const bool hit = static_cast<double>(zv[k]) > L;
+        const unsigned long long ball = __ballot(hit);
+        const int sidx = nc + __popcll(ball & below);
+        if (hit && sidx < CSEG) {
+          cand[wave * CSEG + sidx] = zv[k];
+          cpos[wave * CSEG + sidx] = zp[k];
         }
+        nc += __popcll(ball);
+        const int jj = (s0 + k * NW) * ppw + sub;
+        if (listed && t == 0 && jj < n_pg) dslot[jj] = zs[k];
+      }
     }
+    if (lane == 0) s_ccnt[wave] = nc;
   }
   lds_barrier();
-  const int ncand_all = s_ncand;
-  const bool staged = ncand_all <= kTauCandCap;
+  bool staged = true;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) staged &= s_ccnt[w] <= CSEG;
   // Visit every candidate z > L: from LDS when staged, else from memory.
   auto for_candidates = [&](auto fn) {
     if (staged) {
-      for (int i = tid; i < ncand_all; i += kTauThreads) fn(cand[i]);
+      for (int w = 0; w < NW; ++w)
+        for (int i = tid; i < s_ccnt[w]; i += kTauThreads) fn(cand[w * CSEG + i]);
     } else {
       const int span = n_pg * P;
       for (int fi = tid; fi < span; fi += kTauThreads) {
@@ -602,6 +649,109 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     }
   };
 
+  double t_rel = 0.0;  // tau - M
+  bool solved = false;
+  double blo = L, bhi = Md;  // bracket for the fallback
+
+  // Exact solve by support iteration (r in {1, 2}, candidates staged), by
+  // wave 0 alone.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
+  // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
+  // over S(t) = {y > t}, the count K, sum y and sum y^2, and finds min_S y.
+  // The closed form t* of tau for the support S (sparsemax: (sum y - 1)/K;
+  // 1.5-entmax: the smaller root of sum_S (y - t)^2 = 1) is tau itself when
+  // t* < min_S y, since then S(t*) = S.  Otherwise t moves up: for r = 1 to
+  // t* (over a superset of the support the terms below tau are negative, so
+  // t* <= tau: Michelot's iteration), for r = 2 by a Newton step on
+  // F^(1/2) - 1 (convex, so the step stays below tau).  Lanes sum their
+  // candidates segment by segment in a fixed order and the wave reduces in
+  // a fixed pattern, so the result is the same on every run.
+  if (staged && (r == 1 || r == 2)) {
+    if (wave == 0) {
+      // Up to R * kWave candidates are held in registers: candidate e (in
+      // segment order) goes to lane e % 64, slot e / 64.
+      // Segment starts in scalar registers (wave-uniform), so that locating
+      // a candidate is a compare chain rather than dependent LDS reads.
+      constexpr int R = 16;
+      int segs[NW + 1];
+      segs[0] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        segs[w + 1] = segs[w] + __builtin_amdgcn_readfirstlane(s_ccnt[w]);
+      const int n_all = segs[NW];
+      const bool in_regs = n_all <= R * kWave;
+      float yr[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int e = lane + k * kWave;
+        yr[k] = -INFINITY;
+        if (in_regs && e < n_all) {
+          int base = 0, w = 0;
+#pragma unroll
+          for (int v = 1; v < NW; ++v)
+            if (e >= segs[v]) { w = v; base = segs[v]; }
+          yr[k] = cand[w * CSEG + (e - base)];
+        }
+      }
+      double t = L - Md, res = 0.0;
+      bool ok = false;
+      for (int it = 0; it < kTauIters; ++it) {
+        int K = 0;
+        double SY = 0.0, SY2 = 0.0;
+        float zmin = FLT_MAX;
+        auto visit = [&](float zc) {  // branch-free
+          const double y = static_cast<double>(zc) - Md;
+          const bool in = y > t;
+          const double yy = in ? y : 0.0;
+          K += in ? 1 : 0;
+          SY += yy;
+          SY2 = fma(yy, yy, SY2);
+          zmin = in ? fminf(zmin, zc) : zmin;
+        };
+        if (in_regs) {
+#pragma unroll
+          for (int k = 0; k < R; ++k) visit(yr[k]);
+        } else {
+          for (int w = 0; w < NW; ++w)
+            for (int i = lane; i < s_ccnt[w]; i += kWave) visit(cand[w * CSEG + i]);
+        }
+        K = group_sum_i<kWave>(K);
+        SY = group_sum_d<kWave>(SY);
+        SY2 = group_sum_d<kWave>(SY2);
+        zmin = -group_max<kWave>(-zmin);
+        if (K == 0) break;
+        const double kd = static_cast<double>(K);
+        const double ymin = static_cast<double>(zmin) - Md;
+        double tn;
+        if (r == 1) {
+          tn = (SY - 1.0) / kd;
+          if (tn < ymin) { res = tn; ok = true; break; }
+        } else {
+          const double disc = SY * SY - kd * (SY2 - 1.0);
+          if (disc >= 0.0) {
+            const double ts = (SY - sqrt(disc)) / kd;
+            if (ts < ymin) { res = ts; ok = true; break; }
+          }
+          const double F = SY2 - 2.0 * t * SY + kd * t * t;
+          const double Dv = SY - kd * t;
+          tn = t + (F - sqrt(F)) / Dv;
+        }
+        if (!(tn > t)) {  // converged to rounding without a clean support
+          res = t;
+          ok = true;
+          break;
+        }
+        t = tn;
+      }
+      if (lane == 0) {
+        s_wsolved = ok ? 1 : 0;
+        s_wtau = res;
+      }
+    }
+    lds_barrier();
+    solved = s_wsolved != 0;
+    t_rel = s_wtau;
+  }
+
   // Bin width: the smallest power of two w with NB * w >= M - L.
   double w = 1.0;
   for (int it = 0; it < 64 && w * kTauBins < Md - L; ++it) w *= 2.0;
@@ -612,10 +762,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     return x < kTauBins ? (x > 0.0 ? static_cast<int>(x) : 0) : kTauBins - 1;
   };
 
-  double t_rel = 0.0;  // tau - M
-  bool solved = false;
-  double blo = L, bhi = Md;  // bracket for the fallback
-  if (r == 1 || r == 2) {
+  if (!solved && (r == 1 || r == 2)) {
     for (int i = tid; i < kTauBins; i += kTauThreads) hist[i] = 0u;
     lds_barrier();
     for_candidates([&](float z) { atomicAdd(&hist[bin_of(z)], 1u); });
@@ -732,10 +879,101 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     }
     t_rel = 0.5 * (lo + hi) - Md;
   }
+  const float tau = static_cast<float>(Md + t_rel);
   if (tid == 0) {
-    const float tau = static_cast<float>(Md + t_rel);
     tau_ws[ug] = tau;
     if (tau_user) tau_user[ug] = tau;
+  }
+
+  // Weighted value sum over the support, when every candidate is staged
+  // (the support, z > tau, is among them): p = max(z - tau, 0)^r as in the
+  // chunked path, value rows gathered through the page table.  Each wave
+  // compacts its own segment in place to (p, position) of the support, then
+  // reads its rows with D/8 lanes per row and many rows in flight.  Sums run
+  // in a fixed order, so the result is the same on every run.  Heads done
+  // here are only divided out by the apply step.
+  if (!staged) {
+    if (tid == 0) done[ug] = 0;
+    return;
+  }
+  constexpr int LPT = D / 8, TPW = kWave / LPT, RU = 8;
+  const int h = u % H, b = u / H;
+  const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
+  int nk = 0;
+  {
+    const int nc = s_ccnt[wave];
+    for (int i0 = 0; i0 < nc; i0 += kWave) {
+      const int i = i0 + lane;
+      float pv = 0.f;
+      int pos = 0;
+      if (i < nc) {
+        pv = pow_r(fmaxf(cand[wave * CSEG + i] - tau, 0.f), r, rg);
+        pos = cpos[wave * CSEG + i];
+      }
+      const bool keep = pv > 0.f;
+      const unsigned long long ball = __ballot(keep);
+      if (keep) {
+        const int k = nk + __popcll(ball & below);
+        cand[wave * CSEG + k] = pv;  // k <= i: written after this chunk's reads
+        cpos[wave * CSEG + k] = pos;
+      }
+      nk += __popcll(ball);
+    }
+  }
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float psum = 0.f;
+  for (int base = 0; base < nk; base += TPW * RU) {
+    float x[RU][8];
+    float pw[RU];
+#pragma unroll
+    for (int rr = 0; rr < RU; ++rr) {
+      const int k = base + rr * TPW + sub;
+      pw[rr] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[rr][j] = 0.f;
+      if (k < nk) {
+        pw[rr] = cand[wave * CSEG + k];
+        const int pos = cpos[wave * CSEG + k];
+        const int jj = pos / P, t = pos - jj * P;
+        const int slot =
+            listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
+        load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RU; ++rr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(pw[rr], x[rr][j], acc[j]);
+      if (li == 0) psum += pw[rr];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v = acc[j];
+#pragma unroll
+    for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+    acc[j] = v;
+  }
+  psum = group_sum<kWave>(psum);
+  if (sub == 0)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_vacc[wave][d0 + j] = acc[j];
+  if (lane == 0) s_vsum[wave] = psum;
+  lds_barrier();
+  for (int d = tid; d < D; d += kTauThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += s_vacc[w][d];
+    head_o[static_cast<size_t>(ug) * D + d] = v;
+  }
+  if (tid == 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += s_vsum[w];
+    head_s[ug] = v;
+    done[ug] = 1;
   }
 }
 
@@ -787,7 +1025,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
     int cap, int maxch, int r, float rg, const float *__restrict__ zbuf,
     const float *__restrict__ pmax, const float *__restrict__ tau,
     float *__restrict__ part_o, float *__restrict__ part_s,
-    float *__restrict__ probs) {
+    float *__restrict__ probs, const int32_t *__restrict__ done) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   constexpr int ROWS_STEP = kDecWaves * TPW * kRowUnroll;
@@ -800,8 +1038,10 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
   __shared__ float s_acc[kDecWaves][G][D];
   __shared__ float s_sp[kDecWaves][G];
   const int ppc = kChunkTokens / P;
-  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
-                                                   count, units, H, P, ppc);
+  // Units whose query heads were all finished by the threshold step are
+  // skipped (done == NULL: none is).
+  const int total = build_unit_prefix<kDecThreads>(
+      pref, tmp, seq_lens, sel, count, units, H, P, ppc, done, G);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
   const int Hq = H * G;
@@ -945,13 +1185,20 @@ __global__ __launch_bounds__(kCombThreads) void k_entmax_combine(
     const int32_t *__restrict__ count, int H, int G, int D, int P,
     int max_pages, int maxch, const float *__restrict__ pmax,
     const float *__restrict__ tau, const float *__restrict__ part_o,
-    const float *__restrict__ part_s, float *__restrict__ out) {
+    const float *__restrict__ part_s, const float *__restrict__ head_o,
+    const float *__restrict__ head_s, const int32_t *__restrict__ done,
+    float *__restrict__ out) {
   __shared__ int act[kCombActCap];
   __shared__ int red_i[kCombThreads / kWave];
   __shared__ float s_o[kCombThreads];
   __shared__ float s_s[kCombThreads];
   const int ug = blockIdx.x, u = ug / G, g = ug % G;
   const int tid = threadIdx.x;
+  if (done && done[ug]) {  // summed over the support by the threshold step
+    if (tid < D) out[static_cast<size_t>(ug) * D + tid] =
+        head_o[static_cast<size_t>(ug) * D + tid] / head_s[ug];
+    return;
+  }
   const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   const int ppc = kChunkTokens / P;
   const int nch = (cnt + ppc - 1) / ppc;
@@ -1541,6 +1788,7 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
   const int cap = kv.max_pages * kv.page_size;
   float *z = reinterpret_cast<float *>(w + L.z);
   float *pm = reinterpret_cast<float *>(w + L.cmax);
+  int32_t *sl = reinterpret_cast<int32_t *>(w + L.slot);
   const float zs = (alpha - 1.0f) * scale;
   if constexpr (sizeof(typename E::T) == 2) {
     const uint16_t *k = static_cast<const uint16_t *>(kv.k);
@@ -1549,19 +1797,19 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
         hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 16>), dim3(blocks),
                            dim3(kDecThreads), 0, stream, k, kv.page_table,
                            kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
         break;
       case 32:
         hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 32>), dim3(blocks),
                            dim3(kDecThreads), 0, stream, k, kv.page_table,
                            kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
         break;
       default:
         hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 64>), dim3(blocks),
                            dim3(kDecThreads), 0, stream, k, kv.page_table,
                            kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm);
+                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
         break;
     }
   } else {
@@ -1569,12 +1817,12 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                        dim3(kDecThreads), 0, stream,
                        static_cast<const typename E::T *>(kv.k), kv.page_table,
                        kv.seq_lens, sel, count, q, zs, units, kv.num_kv_heads,
-                       kv.page_size, kv.max_pages, cap, z, pm);
+                       kv.page_size, kv.max_pages, cap, z, pm, sl);
   }
   return hipGetLastError();
 }
 
-template <int G>
+template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,
                                    float *tau, void *ws, hipStream_t stream) {
@@ -1582,13 +1830,18 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
   char *w = static_cast<char *>(ws);
   float rg;
   const int r = exponent_code(alpha, rg);
-  hipLaunchKernelGGL(k_entmax_tau, dim3(kv.batch * kv.num_kv_heads * G),
+  hipLaunchKernelGGL((k_entmax_tau<E, D>), dim3(kv.batch * kv.num_kv_heads * G),
                      dim3(kTauThreads), 0, stream,
                      reinterpret_cast<const float *>(w + L.z),
-                     reinterpret_cast<const float *>(w + L.cmax), kv.seq_lens,
-                     sel, count, kv.num_kv_heads, G, kv.page_size,
+                     reinterpret_cast<const float *>(w + L.cmax),
+                     static_cast<const typename E::T *>(kv.v), kv.page_table,
+                     kv.seq_lens, sel, count, kv.num_kv_heads, G, kv.page_size,
                      kv.max_pages, kv.max_pages * kv.page_size, r, rg,
-                     reinterpret_cast<float *>(w + L.tau), tau);
+                     reinterpret_cast<float *>(w + L.tau), tau,
+                     reinterpret_cast<float *>(w + L.head_o),
+                     reinterpret_cast<float *>(w + L.head_s),
+                     reinterpret_cast<int32_t *>(w + L.done),
+                     reinterpret_cast<const int32_t *>(w + L.slot));
   return hipGetLastError();
 }
 
@@ -1610,6 +1863,10 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
     hipLaunchKernelGGL(k_fill_probs, g, dim3(256), 0, stream, kv.seq_lens,
                        kv.num_kv_heads * G, pstride, probs);
   }
+  // With the debug probabilities every chunk is visited (they are written
+  // there); otherwise heads finished by the threshold step are skipped.
+  const int32_t *done =
+      probs ? nullptr : reinterpret_cast<const int32_t *>(w + L.done);
   const int blocks = persistent_blocks(static_cast<size_t>(units) * mc, 4);
   hipLaunchKernelGGL((k_entmax_apply<E, D, G>), dim3(blocks),
                      dim3(kDecThreads), 0, stream,
@@ -1620,7 +1877,7 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<const float *>(w + L.cmax),
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<float *>(w + L.part_o),
-                     reinterpret_cast<float *>(w + L.part_s), probs);
+                     reinterpret_cast<float *>(w + L.part_s), probs, done);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_entmax_combine, dim3(units * G), dim3(kCombThreads), 0,
@@ -1629,7 +1886,9 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<const float *>(w + L.cmax),
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<const float *>(w + L.part_o),
-                     reinterpret_cast<const float *>(w + L.part_s), out);
+                     reinterpret_cast<const float *>(w + L.part_s),
+                     reinterpret_cast<const float *>(w + L.head_o),
+                     reinterpret_cast<const float *>(w + L.head_s), done, out);
   return hipGetLastError();
 }
 
@@ -1677,6 +1936,9 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
   template hipError_t launch_entmax_scores<E, D, G>(                         \
       const ekv_paged_kv &, const float *, float, float, const int32_t *,    \
       const int32_t *, void *, hipStream_t);                                 \
+  template hipError_t launch_entmax_threshold<E, D, G>(                      \
+      const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
+      void *, hipStream_t);                                                  \
   template hipError_t launch_entmax_apply<E, D, G>(                          \
       const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
       float *, void *, hipStream_t);                                         \
@@ -1685,10 +1947,5 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
       const int32_t *, float *, float *, void *, hipStream_t);
 EKV_FOR_EACH_EDG(EKV_INST_DEC)
 
-#define EKV_INST_TAU(G)                                                      \
-  template hipError_t launch_entmax_threshold<G>(                            \
-      const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
-      void *, hipStream_t);
-EKV_FOR_EACH_G(EKV_INST_TAU)
 
 }  // namespace ekv

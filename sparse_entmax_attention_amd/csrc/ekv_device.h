@@ -97,16 +97,42 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (W >= 64) x = fmaxf(x, __shfl_xor(x, 32, kWave));
   return x;
 }
+// 64-bit values move through DPP as two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long v = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(v >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(static_cast<unsigned int>(hi)) << 32) |
+      static_cast<unsigned int>(lo)));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+// The pairings are symmetric, so every lane of the group ends with the
+// bitwise same sum.
 template <int W>
 __device__ __forceinline__ double group_sum_d(double x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two");
+  if constexpr (W >= 16) x += dpp_d<kDppRowMirror>(x);
+  if constexpr (W >= 8) x += dpp_d<kDppRowHalfMirror>(x);
+  if constexpr (W >= 4) x += dpp_d<kDppQuad2301>(x);
+  if constexpr (W >= 2) x += dpp_d<kDppQuad1032>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, kWave);
   return x;
 }
 template <int W>
 __device__ __forceinline__ int group_sum_i(int x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two");
+  if constexpr (W >= 16) x += dpp_i<kDppRowMirror>(x);
+  if constexpr (W >= 8) x += dpp_i<kDppRowHalfMirror>(x);
+  if constexpr (W >= 4) x += dpp_i<kDppQuad2301>(x);
+  if constexpr (W >= 2) x += dpp_i<kDppQuad1032>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, kWave);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, kWave);
   return x;
 }
 
