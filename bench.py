@@ -88,6 +88,38 @@ class DeviceEvents:
         self.pool = []
 
 
+TRAFFIC_FILE = os.path.join(REPO, "profiles", "hbm_traffic_cluster_1m.txt")
+KERNEL_SOURCES = ("decode.hip", "ekv_device.h", "ekv_kernels.h")
+
+
+def kernel_source_hash():
+    """sha256 over the sources the key-pass kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(REPO, "sparse_entmax_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled), or None when there is none or the
+    kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel") != kernel or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,7 +370,9 @@ def main():
     achieved = kb[dom] / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": (measured_traffic("k_entmax_scores_mfma")
+                            if dom == "entmax_scores" and head_name == "gauss" else None),
                 "bytes_per_launch": kb[dom], "avg_launch_ms": dom_ms}
 
     speedups = {}
