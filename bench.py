@@ -221,7 +221,7 @@ def main():
             ("entmax_scores", lambda: ekv.ekv_entmax_scores(
                 kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
             ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
-                kv, alpha, buf.sel, buf.count, buf.tau, buf.ws_decode)),
+                kv, alpha, buf.sel, buf.count, buf.tau, buf.out, buf.ws_decode)),
             ("entmax_apply", lambda: ekv.ekv_entmax_apply(
                 kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
         ],
@@ -232,7 +232,7 @@ def main():
             ("entmax_scores", lambda: ekv.ekv_entmax_scores(
                 kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
             ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
-                kv, alpha, buf.sel, buf.count, buf.tau, buf.ws_decode)),
+                kv, alpha, buf.sel, buf.count, buf.tau, buf.out, buf.ws_decode)),
             ("entmax_apply", lambda: ekv.ekv_entmax_apply(
                 kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
         ],
@@ -240,7 +240,7 @@ def main():
             ("entmax_scores", lambda: ekv.ekv_entmax_scores(
                 kv, q, buf.scale, alpha, None, None, buf.ws_decode)),
             ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
-                kv, alpha, None, None, buf.tau, buf.ws_decode)),
+                kv, alpha, None, None, buf.tau, buf.out, buf.ws_decode)),
             ("entmax_apply", lambda: ekv.ekv_entmax_apply(
                 kv, alpha, None, None, buf.out, None, buf.ws_decode)),
         ],

@@ -221,9 +221,13 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
  *   ekv_entmax_scores     gathers the selected keys and writes z to the
  *                         workspace with per-chunk maxima.
  *   ekv_entmax_threshold  solves tau per query head (tau may be NULL: it is
- *                         then kept in the workspace only).
- *   ekv_entmax_apply      reads values only for tokens with p_i > 0 and
- *                         writes out (and probs if not NULL).
+ *                         then kept in the workspace only) and, for every
+ *                         head whose candidate scores fit on chip (the usual
+ *                         case), gathers the values of the support and
+ *                         writes that head's row of out.
+ *   ekv_entmax_apply      writes the remaining rows of out (all rows, and
+ *                         probs, when probs is not NULL), reading values
+ *                         only for tokens with p_i > 0.
  */
 ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,
@@ -231,8 +235,8 @@ ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
                              void *stream);
 ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
                                 const int32_t *sel, const int32_t *count,
-                                float *tau, void *ws, size_t ws_bytes,
-                                void *stream);
+                                float *tau, float *out, void *ws,
+                                size_t ws_bytes, void *stream);
 ekv_status ekv_entmax_apply(const ekv_paged_kv *kv, float alpha,
                             const int32_t *sel, const int32_t *count,
                             float *out, float *probs, void *ws,

@@ -71,7 +71,8 @@ _SIGNATURES = {
     "ekv_entmax_scores": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
                                    _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
     "ekv_entmax_threshold": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_f32,
-                                      _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_size,
+                                      _c_p]),
     "ekv_entmax_apply": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_f32, _c_p,
                                   _c_p, _c_p, _c_p, _c_p, _c_size, _c_p]),
     "ekv_softmax_decode": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
@@ -250,12 +251,12 @@ def ekv_entmax_scores(kv: PagedKV, q, scale: float, alpha: float, sel, count,
         "ekv_entmax_scores")
 
 
-def ekv_entmax_threshold(kv: PagedKV, alpha: float, sel, count, tau, ws,
+def ekv_entmax_threshold(kv: PagedKV, alpha: float, sel, count, tau, out, ws,
                          stream=None) -> None:
     s = kv.struct()
     _check(load_library().ekv_entmax_threshold(
         ctypes.byref(s), float(alpha), _ptr(sel), _ptr(count), _ptr(tau),
-        _ptr(ws), ws.numel(), _stream(stream)), "ekv_entmax_threshold")
+        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "ekv_entmax_threshold")
 
 
 def ekv_entmax_apply(kv: PagedKV, alpha: float, sel, count, out, probs, ws,

@@ -278,16 +278,17 @@ ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
 
 ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
                                 const int32_t *sel, const int32_t *count,
-                                float *tau, void *ws, size_t ws_bytes,
-                                void *stream) {
+                                float *tau, float *out, void *ws,
+                                size_t ws_bytes, void *stream) {
   EKV_TRY(check_kv(kv, false, true));
   EKV_TRY(check_alpha(alpha));
   EKV_TRY(check_sel(sel, count));
+  if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
   EKV_TRY(check_ws(ws, ws_bytes, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0)));
   const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
     return ekv::launch_entmax_threshold<decltype(E), decltype(D)::value,
                                         decltype(G)::value>(
-        *kv, alpha, sel, count, tau, ws, as_stream(stream));
+        *kv, alpha, sel, count, tau, out, ws, as_stream(stream));
   });
   return hip_status(e, "ekv_entmax_threshold launch");
 }
@@ -317,7 +318,7 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
   EKV_TRY(check_kv(kv, true, true));
   if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
   EKV_TRY(ekv_entmax_scores(kv, q, scale, alpha, sel, count, ws, ws_bytes, stream));
-  EKV_TRY(ekv_entmax_threshold(kv, alpha, sel, count, tau, ws, ws_bytes, stream));
+  EKV_TRY(ekv_entmax_threshold(kv, alpha, sel, count, tau, out, ws, ws_bytes, stream));
   return ekv_entmax_apply(kv, alpha, sel, count, out, probs, ws, ws_bytes, stream);
 }
 

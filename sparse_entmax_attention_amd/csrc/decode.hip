@@ -42,9 +42,8 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   w.tau = al(w.cmax + units * G * static_cast<size_t>(kv.max_pages) * 4);
   w.part_o = al(w.tau + units * G * 4);
   w.part_s = al(w.part_o + units * mc * G * D * 4);
-  w.head_o = al(w.part_s + units * mc * G * 4);
-  w.head_s = al(w.head_o + units * G * D * 4);
-  w.done = al(w.head_s + units * G * 4);
+  w.ctr = al(w.part_s + units * mc * G * 4);  // chunks finished, per unit
+  w.done = al(w.ctr + units * 4);
   w.slot = al(w.done + units * G * 4);  // pool slot per selected page
   w.total = al(w.slot + units * static_cast<size_t>(kv.max_pages) * 4);
   return w;
@@ -461,8 +460,8 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, int H, int G, int P, int max_pages,
     int cap, int r, float rg, float *__restrict__ tau_ws,
-    float *__restrict__ tau_user, float *__restrict__ head_o,
-    float *__restrict__ head_s, int32_t *__restrict__ done,
+    float *__restrict__ tau_user, float *__restrict__ out,
+    int32_t *__restrict__ done, int32_t *__restrict__ ctr,
     const int32_t *__restrict__ slots) {
   constexpr int NW = kTauThreads / kWave;
   constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
@@ -891,7 +890,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   // compacts its own segment in place to (p, position) of the support, then
   // reads its rows with D/8 lanes per row and many rows in flight.  Sums run
   // in a fixed order, so the result is the same on every run.  Heads done
-  // here are only divided out by the apply step.
+  // here are skipped by the apply step, whose per-unit chunk counter is
+  // reset here for it.
+  if (tid == 0 && ug % G == 0) ctr[u] = 0;
   if (!staged) {
     if (tid == 0) done[ug] = 0;
     return;
@@ -962,19 +963,16 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     for (int j = 0; j < 8; ++j) s_vacc[wave][d0 + j] = acc[j];
   if (lane == 0) s_vsum[wave] = psum;
   lds_barrier();
+  float psum_all = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) psum_all += s_vsum[w];
   for (int d = tid; d < D; d += kTauThreads) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += s_vacc[w][d];
-    head_o[static_cast<size_t>(ug) * D + d] = v;
+    out[static_cast<size_t>(ug) * D + d] = v / psum_all;
   }
-  if (tid == 0) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) v += s_vsum[w];
-    head_s[ug] = v;
-    done[ug] = 1;
-  }
+  if (tid == 0) done[ug] = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,12 +1007,53 @@ __device__ __forceinline__ int stage_chunk(ChunkPages &cp,
 
 // ---------------------------------------------------------------------------
 // 3a. Apply: chunk partials of sum_i p_i v_i and sum_i p_i.  Persistent
-// blocks over chunks.  A chunk none of whose pages has a maximum above tau
-// for any head is skipped.  Otherwise p is computed once per (token, head)
+// blocks over the chunks of the units the threshold step did not finish.
+// A chunk none of whose pages has a maximum above tau for any head only
+// records a zero partial.  Otherwise p is computed once per (token, head)
 // into LDS from the z of the chunk's active pages, the rows with some p > 0
-// are compacted, and all their value loads are issued together.
+// are compacted, and all their value loads are issued together.  The block
+// that completes a unit's last chunk merges the unit's partials.
 // ---------------------------------------------------------------------------
 constexpr int kRowUnroll = 4;
+
+// Merge of one unit's chunk partials: out = sum_c o_c / sum_c s_c over the
+// chunks with some p > 0 (the others add exact zeros), in chunk order, for
+// every query head not already finished by the threshold step.  One block;
+// `list` holds kChunkTokens ints and `tmp` kDecWaves ints.
+template <int G, int D>
+__device__ void merge_unit_partials(int u, int nch, int maxch,
+                                    const float *part_o, const float *part_s,
+                                    const int32_t *done, float *out, int *list,
+                                    int *tmp) {
+  int nact = 0;
+  for (int base = 0; base < nch; base += kDecThreads) {
+    const int c = base + threadIdx.x;
+    bool flag = false;
+    if (c < nch)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        flag |= part_s[(static_cast<size_t>(u) * maxch + c) * G + g] > 0.f;
+    int tot;
+    const int rk = tile_rank<kDecThreads>(flag, tmp, tot);
+    if (flag && nact + rk < kChunkTokens) list[nact + rk] = c;
+    nact += tot;
+  }
+  lds_barrier();
+  const bool listed = nact <= kChunkTokens;
+  const int n = listed ? nact : nch;
+  for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
+    const int g = e / D, d = e - g * D;
+    if (done && done[u * G + g]) continue;
+    float o = 0.f, sum = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const int c = listed ? list[k] : k;
+      const size_t cb = static_cast<size_t>(u) * maxch + c;
+      o += part_o[(cb * G + g) * D + d];
+      sum += part_s[cb * G + g];
+    }
+    out[(static_cast<size_t>(u) * G + g) * D + d] = o / sum;
+  }
+}
 
 template <class E, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
@@ -1025,7 +1064,8 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
     int cap, int maxch, int r, float rg, const float *__restrict__ zbuf,
     const float *__restrict__ pmax, const float *__restrict__ tau,
     float *__restrict__ part_o, float *__restrict__ part_s,
-    float *__restrict__ probs, const int32_t *__restrict__ done) {
+    float *__restrict__ probs, const int32_t *__restrict__ done,
+    int32_t *__restrict__ ctr, float *__restrict__ out) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   constexpr int ROWS_STEP = kDecWaves * TPW * kRowUnroll;
@@ -1037,6 +1077,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
   __shared__ int s_rows[kChunkTokens];
   __shared__ float s_acc[kDecWaves][G][D];
   __shared__ float s_sp[kDecWaves][G];
+  __shared__ int s_last;
   const int ppc = kChunkTokens / P;
   // Units whose query heads were all finished by the threshold step are
   // skipped (done == NULL: none is).
@@ -1064,7 +1105,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
                tau[u * G + g];
       s_act[jj] = act;
     }
-    if (!__syncthreads_or(act)) continue;
+    if (__syncthreads_or(act)) {
     stage_chunk(cp, page_table, seq_lens, sel, u, c, cnt, H, P, max_pages);
     float tg[G];
 #pragma unroll
@@ -1168,88 +1209,27 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
       for (int ww = 1; ww < kDecWaves; ++ww) v += s_sp[ww][threadIdx.x];
       part_s[(static_cast<size_t>(u) * maxch + c) * G + threadIdx.x] = v;
     }
-    lds_barrier();
+    } else if (threadIdx.x < G) {  // no page of the chunk can hold p > 0
+      part_s[(static_cast<size_t>(u) * maxch + c) * G + threadIdx.x] = 0.f;
+    }
+    // The block that finishes the unit's last chunk merges its partials
+    // (in chunk order) into out.
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = atomicAdd(&ctr[u], 1) == pref[u + 1] - pref[u] - 1;
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      merge_unit_partials<G, D>(u, pref[u + 1] - pref[u], maxch, part_o, part_s,
+                                done, out, s_rows, tmp);
+      if (threadIdx.x == 0) ctr[u] = 0;
+    }
+    __syncthreads();  // LDS of this chunk is reused by the next one
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3b. Merge chunk partials in chunk order: out = sum_c o_c / sum_c s_c over
-// the chunks holding a page whose maximum exceeds tau for this head (every
-// other chunk contributes exact zeros).  One block per query head.
-// ---------------------------------------------------------------------------
-constexpr int kCombThreads = 1024;
-constexpr int kCombActCap = 4096;
-
-__global__ __launch_bounds__(kCombThreads) void k_entmax_combine(
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, int H, int G, int D, int P,
-    int max_pages, int maxch, const float *__restrict__ pmax,
-    const float *__restrict__ tau, const float *__restrict__ part_o,
-    const float *__restrict__ part_s, const float *__restrict__ head_o,
-    const float *__restrict__ head_s, const int32_t *__restrict__ done,
-    float *__restrict__ out) {
-  __shared__ int act[kCombActCap];
-  __shared__ int red_i[kCombThreads / kWave];
-  __shared__ float s_o[kCombThreads];
-  __shared__ float s_s[kCombThreads];
-  const int ug = blockIdx.x, u = ug / G, g = ug % G;
-  const int tid = threadIdx.x;
-  if (done && done[ug]) {  // summed over the support by the threshold step
-    if (tid < D) out[static_cast<size_t>(ug) * D + tid] =
-        head_o[static_cast<size_t>(ug) * D + tid] / head_s[ug];
-    return;
-  }
-  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
-  const int ppc = kChunkTokens / P;
-  const int nch = (cnt + ppc - 1) / ppc;
-  const float t = tau[ug];
-  const float *pm = pmax + static_cast<size_t>(ug) * max_pages;
-  int nact = 0;
-  for (int base = 0; base < nch; base += kCombThreads) {
-    const int c = base + tid;
-    bool flag = false;
-    if (c < nch) {
-      const int j1 = min(cnt, (c + 1) * ppc);
-      for (int j = c * ppc; j < j1; ++j) flag |= pm[j] > t;
-    }
-    int tot;
-    const int rk = tile_rank<kCombThreads>(flag, red_i, tot);
-    if (flag && nact + rk < kCombActCap) act[nact + rk] = c;
-    nact += tot;
-  }
-  lds_barrier();
-  const bool listed = nact <= kCombActCap;
-  const int slices = kCombThreads / D;
-  const int d = tid % D, sl = tid / D;
-  float o = 0.f, s = 0.f;
-  const int n = listed ? nact : nch;
-  for (int k = sl; k < n; k += slices) {
-    int c = k;
-    if (listed) {
-      c = act[k];
-    } else {
-      const int j1 = min(cnt, (c + 1) * ppc);
-      bool any = false;
-      for (int j = c * ppc; j < j1; ++j) any |= pm[j] > t;
-      if (!any) continue;
-    }
-    const size_t base = static_cast<size_t>(u) * maxch + c;
-    o += part_o[(base * G + g) * D + d];
-    if (d == 0) s += part_s[base * G + g];
-  }
-  s_o[tid] = o;
-  s_s[tid] = s;
-  lds_barrier();
-  if (tid < D) {
-    float oo = 0.f, ss = 0.f;
-    for (int k = 0; k < slices; ++k) {
-      oo += s_o[k * D + tid];
-      ss += s_s[k * D];
-    }
-    out[static_cast<size_t>(ug) * D + tid] = oo / ss;
-  }
-}
-
 // Zero probs[b][h][0 .. seq_lens[b]) for the debug output.
 __global__ void k_fill_probs(const int32_t *__restrict__ seq_lens, int Hq,
                              size_t stride, float *__restrict__ probs) {
@@ -1825,7 +1805,8 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
 template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,
-                                   float *tau, void *ws, hipStream_t stream) {
+                                   float *tau, float *out, void *ws,
+                                   hipStream_t stream) {
   const DecodeWs L = decode_ws_layout(kv);
   char *w = static_cast<char *>(ws);
   float rg;
@@ -1837,10 +1818,9 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                      static_cast<const typename E::T *>(kv.v), kv.page_table,
                      kv.seq_lens, sel, count, kv.num_kv_heads, G, kv.page_size,
                      kv.max_pages, kv.max_pages * kv.page_size, r, rg,
-                     reinterpret_cast<float *>(w + L.tau), tau,
-                     reinterpret_cast<float *>(w + L.head_o),
-                     reinterpret_cast<float *>(w + L.head_s),
+                     reinterpret_cast<float *>(w + L.tau), tau, out,
                      reinterpret_cast<int32_t *>(w + L.done),
+                     reinterpret_cast<int32_t *>(w + L.ctr),
                      reinterpret_cast<const int32_t *>(w + L.slot));
   return hipGetLastError();
 }
@@ -1877,18 +1857,8 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<const float *>(w + L.cmax),
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<float *>(w + L.part_o),
-                     reinterpret_cast<float *>(w + L.part_s), probs, done);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_entmax_combine, dim3(units * G), dim3(kCombThreads), 0,
-                     stream, kv.seq_lens, sel, count, kv.num_kv_heads, G, D,
-                     kv.page_size, kv.max_pages, mc,
-                     reinterpret_cast<const float *>(w + L.cmax),
-                     reinterpret_cast<const float *>(w + L.tau),
-                     reinterpret_cast<const float *>(w + L.part_o),
-                     reinterpret_cast<const float *>(w + L.part_s),
-                     reinterpret_cast<const float *>(w + L.head_o),
-                     reinterpret_cast<const float *>(w + L.head_s), done, out);
+                     reinterpret_cast<float *>(w + L.part_s), probs, done,
+                     reinterpret_cast<int32_t *>(w + L.ctr), out);
   return hipGetLastError();
 }
 
@@ -1938,7 +1908,7 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
       const int32_t *, void *, hipStream_t);                                 \
   template hipError_t launch_entmax_threshold<E, D, G>(                      \
       const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
-      void *, hipStream_t);                                                  \
+      float *, void *, hipStream_t);                                         \
   template hipError_t launch_entmax_apply<E, D, G>(                          \
       const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
       float *, void *, hipStream_t);                                         \

@@ -37,7 +37,7 @@ inline int max_chunks(const ekv_paged_kv &kv) {
 
 // Decode workspace layout (offsets in bytes, each 256-byte aligned).
 struct DecodeWs {
-  size_t z, cmax, tau, part_o, part_s, head_o, head_s, done, slot, total;
+  size_t z, cmax, tau, part_o, part_s, ctr, done, slot, total;
 };
 DecodeWs decode_ws_layout(const ekv_paged_kv &kv);
 struct SoftmaxWs {
@@ -70,7 +70,8 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
 template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,
-                                   float *tau, void *ws, hipStream_t stream);
+                                   float *tau, float *out, void *ws,
+                                   hipStream_t stream);
 template <class E, int D, int G>
 hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                                const int32_t *sel, const int32_t *count,
