@@ -46,6 +46,28 @@ __device__ __forceinline__ void load8(const uint16_t *p, float (&x)[8]) {
   x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
 }
 
+// The 8 coordinates owned by lane li of a group of D/8 lanes that shares a
+// row.  A 32-bit row is read as [4 li, 4 li + 4) and [D/2 + 4 li, ...): each
+// of the lane's two 16-byte loads is then part of one contiguous span of the
+// row across the group.  A 16-bit row is read as 8 consecutive values (one
+// 16-byte load).  coord_of gives the coordinate of the lane's j-th value.
+template <class T, int D>
+__device__ __forceinline__ int coord_of(int li, int j) {
+  if constexpr (sizeof(T) == 4) return j < 4 ? 4 * li + j : D / 2 + 4 * li + (j - 4);
+  else return 8 * li + j;
+}
+template <int D>
+__device__ __forceinline__ void load8_lane(const float *row, int li, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(row + 4 * li);
+  const float4 b = *reinterpret_cast<const float4 *>(row + D / 2 + 4 * li);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <int D>
+__device__ __forceinline__ void load8_lane(const uint16_t *row, int li, float (&x)[8]) {
+  load8(row + 8 * li, x);
+}
+
 __device__ __forceinline__ float load1(const float *p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t *p) {
   return __uint_as_float(static_cast<uint32_t>(*p) << 16);

@@ -8,6 +8,8 @@
 // (Gaussian) per record.  Both are HBM-bound.
 #include <float.h>
 
+#include <algorithm>
+
 #include "ekv_device.h"
 #include "ekv_kernels.h"
 
@@ -131,57 +133,87 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
 // ---------------------------------------------------------------------------
 constexpr int kScoreTile = kPageTile;  // pages per block
 
-template <class E, int D, int G>
+template <class E, int D, int G, int MODE>
 __global__ __launch_bounds__(256) void k_score(
     const typename E::T *__restrict__ bbox, const float *__restrict__ gauss,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const float *__restrict__ q,
-    float scale, int mode, int H, int P, int max_pages, int batch,
+    float scale, int H, int P, int max_pages, int batch,
     float *__restrict__ ub, float *__restrict__ gstat) {
   constexpr int LPP = D / 8;          // lanes per page
   constexpr int PPW = kWave / LPP;    // pages per wave step
   constexpr int NWAVE = 4;
+  constexpr int NSTEP = kScoreTile / (NWAVE * PPW);
   static_assert(kScoreTile % (NWAVE * PPW) == 0, "tile must fill the waves");
-  const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int sub = lane / LPP, li = lane % LPP, d0 = li * 8;
-  const int len = seq_lens[b];
-  const int np = n_pages_of(len, P);
-  const int tile0 = blockIdx.x * kScoreTile;
-  if (tile0 >= np) return;
+  const int sub = lane / LPP, li = lane % LPP;
   const int Hq = H * G;
   const int n_tiles = (max_pages + kScoreTile - 1) / kScoreTile;
+  const int n_items = batch * H * n_tiles;
   __shared__ float s_tile[4][3 * G + 1];
 
-  float qp[G][8], qn[G][8];
+  // Persistent blocks over (sequence, KV head, tile) items.  The page-table
+  // entries of a block's next item are read while the current item is
+  // scored, so only the first item waits on them before its metadata loads.
+  auto page_of = [&](int tile, int k) {
+    return tile * kScoreTile + (k * NWAVE + wave) * PPW + sub;
+  };
+  auto fetch_slots = [&](int item, int (&raw)[NSTEP]) {
+    const int b = item / (H * n_tiles);
+    const int tile = item % n_tiles;
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
+      const int lp = page_of(tile, k);
+      // entries past the sequence end are in bounds (and unused)
+      raw[k] = lp < max_pages ? page_table[static_cast<size_t>(b) * max_pages + lp] : 0;
+    }
+  };
+  int slot_raw[NSTEP];
+  int item = blockIdx.x;
+  if (item < n_items) fetch_slots(item, slot_raw);
+  for (; item < n_items; item += gridDim.x) {
+    int slot_next[NSTEP];
+    const int nxt = item + gridDim.x;
+    if (nxt < n_items) fetch_slots(nxt, slot_next);
+    const int b = item / (H * n_tiles);
+    const int h = (item / n_tiles) % H;
+    const int tile = item % n_tiles;
+    const int tile0 = tile * kScoreTile;
+    const int len = seq_lens[b];
+    const int np = n_pages_of(len, P);
+    if (tile0 < np) {
+
+  // scale * q at the coordinates this lane owns in a box row (qb) and in a
+  // Gaussian row (qs, float32); see coord_of.
+  float qs[G][8], qb[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float *qg = q + (static_cast<size_t>(b) * Hq + h * G + g) * D + d0;
+    const float *qg = q + (static_cast<size_t>(b) * Hq + h * G + g) * D;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = qg[j] * scale;
-      qp[g][j] = fmaxf(x, 0.f);
-      qn[g][j] = fminf(x, 0.f);
+      if constexpr ((MODE & EKV_SCORE_GAUSS) != 0)
+        qs[g][j] = qg[coord_of<float, D>(li, j)] * scale;
+      if constexpr ((MODE & EKV_SCORE_BBOX) != 0)
+        qb[g][j] = qg[coord_of<typename E::T, D>(li, j)] * scale;
     }
   }
 
-  constexpr int NSTEP = kScoreTile / (NWAVE * PPW);
   int lps[NSTEP], slots[NSTEP];
   bool valid[NSTEP];
 #pragma unroll
   for (int k = 0; k < NSTEP; ++k) {
-    lps[k] = tile0 + (k * NWAVE + wave) * PPW + sub;
+    lps[k] = page_of(tile, k);
     valid[k] = lps[k] < np;
-    slots[k] = valid[k] ? page_table[b * max_pages + lps[k]] : 0;
+    slots[k] = valid[k] ? slot_raw[k] : 0;
   }
-  if (mode & EKV_SCORE_BBOX) {
+  if constexpr ((MODE & EKV_SCORE_BBOX) != 0) {
     float tmax = -FLT_MAX;
     float kmin[NSTEP][8], kmax[NSTEP][8];
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
       if (valid[k]) {
-        load8(bbox + meta_row(slots[k], h, 0, H, D) + d0, kmin[k]);
-        load8(bbox + meta_row(slots[k], h, 1, H, D) + d0, kmax[k]);
+        load8_lane<D>(bbox + meta_row(slots[k], h, 0, H, D), li, kmin[k]);
+        load8_lane<D>(bbox + meta_row(slots[k], h, 1, H, D), li, kmax[k]);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) { kmin[k][j] = 0.f; kmax[k][j] = 0.f; }
@@ -195,8 +227,8 @@ __global__ __launch_bounds__(256) void k_score(
         float a = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          a = fmaf(qp[g][j], kmax[k][j], a);
-          a = fmaf(qn[g][j], kmin[k][j], a);
+          a = fmaf(fmaxf(qb[g][j], 0.f), kmax[k][j], a);
+          a = fmaf(fminf(qb[g][j], 0.f), kmin[k][j], a);
         }
         acc[g] = group_sum<LPP>(a);
       }
@@ -218,10 +250,10 @@ __global__ __launch_bounds__(256) void k_score(
       float m = s_tile[0][3 * G];
       for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, s_tile[w][3 * G]);
       ub[static_cast<size_t>(batch) * Hq * max_pages +
-         (static_cast<size_t>(b) * H + h) * n_tiles + blockIdx.x] = m;
+         (static_cast<size_t>(b) * H + h) * n_tiles + tile] = m;
     }
   }
-  if (mode & EKV_SCORE_GAUSS) {
+  if constexpr ((MODE & EKV_SCORE_GAUSS) != 0) {
     const float cP = sqrtf(2.0f * logf(static_cast<float>(P)));
     float t_mu[G], t_pr[G], t_kp[G];
 #pragma unroll
@@ -230,8 +262,8 @@ __global__ __launch_bounds__(256) void k_score(
 #pragma unroll
     for (int k = 0; k < NSTEP; ++k) {
       if (valid[k]) {
-        load8(gauss + meta_row(slots[k], h, 0, H, D) + d0, mean[k]);
-        load8(gauss + meta_row(slots[k], h, 1, H, D) + d0, var[k]);
+        load8_lane<D>(gauss + meta_row(slots[k], h, 0, H, D), li, mean[k]);
+        load8_lane<D>(gauss + meta_row(slots[k], h, 1, H, D), li, var[k]);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) { mean[k][j] = 0.f; var[k][j] = 0.f; }
@@ -245,7 +277,7 @@ __global__ __launch_bounds__(256) void k_score(
         float a = 0.f, c = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float x = qp[g][j] + qn[g][j];
+          const float x = qs[g][j];
           a = fmaf(x, mean[k][j], a);
           c = fmaf(x * x, var[k][j], c);
         }
@@ -294,8 +326,13 @@ __global__ __launch_bounds__(256) void k_score(
       }
       float4 *gt = reinterpret_cast<float4 *>(
           gstat + gstat_tile_offset(batch, Hq, max_pages));
-      gt[(static_cast<size_t>(b) * Hq + h * G + g) * n_tiles + blockIdx.x] = r4;
+      gt[(static_cast<size_t>(b) * Hq + h * G + g) * n_tiles + tile] = r4;
     }
+  }
+    }
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) slot_raw[k] = slot_next[k];
+    lds_barrier();  // s_tile is rewritten by the next item
   }
 }
 
@@ -320,13 +357,29 @@ template <class E, int D, int G>
 hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
                         const float *q, float scale, int mode, float *ub,
                         float *gstat, hipStream_t stream) {
-  dim3 grid((kv.max_pages + kScoreTile - 1) / kScoreTile, kv.num_kv_heads,
-            kv.batch);
-  hipLaunchKernelGGL((k_score<E, D, G>), grid, dim3(256), 0, stream,
-                     static_cast<const typename E::T *>(meta.bbox), meta.gauss,
-                     kv.page_table, kv.seq_lens, q, scale, mode,
-                     kv.num_kv_heads, kv.page_size, kv.max_pages, kv.batch, ub,
-                     gstat);
+  const int items = ((kv.max_pages + kScoreTile - 1) / kScoreTile) *
+                    kv.num_kv_heads * kv.batch;
+  auto launch = [&](auto kern) {
+    int dev = 0, n_cu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess || n_cu <= 0)
+      n_cu = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(kern), 256, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    const int blocks = std::min(items, n_cu * per_cu);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const typename E::T *>(meta.bbox),
+                       meta.gauss, kv.page_table, kv.seq_lens, q, scale,
+                       kv.num_kv_heads, kv.page_size, kv.max_pages, kv.batch,
+                       ub, gstat);
+  };
+  constexpr int kBoth = EKV_SCORE_BBOX | EKV_SCORE_GAUSS;
+  if (mode == EKV_SCORE_BBOX) launch(k_score<E, D, G, EKV_SCORE_BBOX>);
+  else if (mode == EKV_SCORE_GAUSS) launch(k_score<E, D, G, EKV_SCORE_GAUSS>);
+  else launch(k_score<E, D, G, kBoth>);
   return hipGetLastError();
 }
 
