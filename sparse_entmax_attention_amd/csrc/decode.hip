@@ -39,7 +39,7 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   DecodeWs w;
   w.z = 0;
   w.cmax = al(w.z + units * G * cap * 4);  // per-page maxima
-  w.tau = al(w.cmax + units * G * static_cast<size_t>(kv.max_pages) * 4);
+  w.tau = al(w.cmax + units * G * static_cast<size_t>(pm_stride(kv.max_pages)) * 4);
   w.part_o = al(w.tau + units * G * 4);
   w.part_s = al(w.part_o + units * mc * G * D * 4);
   w.ctr = al(w.part_s + units * mc * G * 4);  // chunks finished, per unit
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
         if (g < G) {
           const float m = group_max<16>(pm[ps][i]);
           if (lane == 0)
-            pmax[(static_cast<size_t>(u) * G + g) * max_pages + cur.j] = m;
+            pmax[(static_cast<size_t>(u) * G + g) * pm_stride(max_pages) + cur.j] = m;
         }
       }
     if (lane == 0) slots[static_cast<size_t>(u) * max_pages + cur.j] = cur.slot;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float m = group_max<kWave>(mx[g]);
-      if (lane == 0) pmax[(static_cast<size_t>(u) * G + g) * max_pages + r.j] = m;
+      if (lane == 0) pmax[(static_cast<size_t>(u) * G + g) * pm_stride(max_pages) + r.j] = m;
     }
     if (lane == 0) slots[static_cast<size_t>(u) * max_pages + r.j] = r.slot;
   }
@@ -489,22 +489,32 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
 
   const int ug = blockIdx.x, u = ug / G;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+  const int mps = pm_stride(max_pages);
   const float *zh = zbuf + static_cast<size_t>(ug) * cap;
-  const float *pm = pmax + static_cast<size_t>(ug) * max_pages;
-  constexpr int U = 32;
+  const float *pm = pmax + static_cast<size_t>(ug) * mps;
+  constexpr int U = 32, U4 = U / 4;
 
-  // Page maxima, read once: thread (wave, lane) holds pages
-  // tid + k * kTauThreads, k < U (one 64-page tile per wave and k); pages
-  // beyond U * kTauThreads (very long selections) are re-read when needed.
+  // Page maxima, read once with 16-byte loads, issued before the page count
+  // is known (rows are padded to a multiple of 4; entries past the count
+  // are masked): thread tid holds pages 4 tid + e + 4 k kTauThreads
+  // (e < 4, k < U/4); pages beyond U * kTauThreads (very long selections)
+  // are re-read when needed.
   static_assert(kTauMaxBins <= kTauBins, "page-maximum bins reuse hist");
   constexpr int CACHED = kTauThreads * U;
+  auto page_k = [&](int k, int e) { return 4 * tid + e + 4 * k * kTauThreads; };
   float pv[U];
 #pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int j = tid + k * kTauThreads;
-    pv[k] = j < cnt ? pm[j] : -FLT_MAX;
+  for (int k = 0; k < U4; ++k) {
+    float4 v = make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
+    if (page_k(k, 0) < mps) v = *reinterpret_cast<const float4 *>(pm + page_k(k, 0));
+    pv[4 * k] = v.x; pv[4 * k + 1] = v.y; pv[4 * k + 2] = v.z; pv[4 * k + 3] = v.w;
   }
+  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+#pragma unroll
+  for (int k = 0; k < U4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (page_k(k, e) >= cnt) pv[4 * k + e] = -FLT_MAX;
   for (int i = tid; i < kTauMaxBins; i += kTauThreads) hist[i] = 0u;
   // Largest score.
   float mloc = -FLT_MAX;
@@ -560,7 +570,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     npw += __popcll(ball);
   };
 #pragma unroll
-  for (int k = 0; k < U; ++k) list_page(tid + k * kTauThreads, pv[k]);
+  for (int k = 0; k < U4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) list_page(page_k(k, e), pv[4 * k + e]);
   for (int jb = CACHED + wave * kWave; jb < cnt; jb += kTauThreads) {
     const int j = jb + lane;
     list_page(j, j < cnt ? pm[j] : -FLT_MAX);
@@ -585,44 +597,48 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
 
   // Stage the candidates z > L in LDS, wave w appending to its own segment
   // cand[w * CSEG ..] in a fixed order (no atomics, so the order does not
-  // change from run to run).  A wave step covers kWave / P listed pages, one
-  // token per lane, with US steps in flight.
+  // change from run to run).  Each lane loads 4 consecutive scores (16 bytes)
+  // of a page, so a wave step covers 4 kWave / P listed pages; US steps are
+  // in flight.
   {
-    constexpr int US = 32;
-    const int ppw = kWave / P, sub = lane / P, t = lane - sub * P;
+    constexpr int US = 8;
+    const int lpp = P / 4, ppw = kWave / lpp;
+    const int sub = lane / lpp, t4 = 4 * (lane - sub * lpp);
     const int steps = (n_pg + ppw - 1) / ppw;
     int nc = 0;
     for (int s0 = wave; s0 < steps; s0 += NW * US) {
-      float zv[US];
-      int zp[US], zs[US];
+      float4 zv[US];
+      int zs[US];
 #pragma unroll
       for (int k = 0; k < US; ++k) {
         const int jj = (s0 + k * NW) * ppw + sub;
-        zv[k] = -INFINITY;
-        zp[k] = 0;
+        zv[k] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         zs[k] = 0;
         if (jj < n_pg) {
           const int j = page_of(jj);
-          zp[k] = jj * P + t;
           if (listed || static_cast<double>(pm[j]) > L)
-            zv[k] = zh[static_cast<size_t>(j) * P + t];
+            zv[k] = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(j) * P + t4);
           // the page's pool slot (written by the score pass), for the
           // value gather at the end; loaded alongside the scores
-          if (listed && t == 0) zs[k] = slots[static_cast<size_t>(u) * max_pages + j];
+          if (listed && t4 == 0) zs[k] = slots[static_cast<size_t>(u) * max_pages + j];
         }
       }
 #pragma unroll
       for (int k = 0; k < US; ++k) {
-        const bool hit = static_cast<double>(zv[k]) > L;
-        const unsigned long long ball = __ballot(hit);
-        const int sidx = nc + __popcll(ball & below);
-        if (hit && sidx < CSEG) {
-          cand[wave * CSEG + sidx] = zv[k];
-          cpos[wave * CSEG + sidx] = zp[k];
-        }
-        nc += __popcll(ball);
         const int jj = (s0 + k * NW) * ppw + sub;
-        if (listed && t == 0 && jj < n_pg) dslot[jj] = zs[k];
+        const float ze[4] = {zv[k].x, zv[k].y, zv[k].z, zv[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool hit = static_cast<double>(ze[e]) > L;
+          const unsigned long long ball = __ballot(hit);
+          const int sidx = nc + __popcll(ball & below);
+          if (hit && sidx < CSEG) {
+            cand[wave * CSEG + sidx] = ze[e];
+            cpos[wave * CSEG + sidx] = jj * P + t4 + e;
+          }
+          nc += __popcll(ball);
+        }
+        if (listed && t4 == 0 && jj < n_pg) dslot[jj] = zs[k];
       }
     }
     if (lane == 0) s_ccnt[wave] = nc;
@@ -744,6 +760,41 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       if (lane == 0) {
         s_wsolved = ok ? 1 : 0;
         s_wtau = res;
+      }
+    } else if (listed) {
+      // Meanwhile the other waves bring the value rows of every candidate
+      // (a superset of the support) into the L2, so that the gather after
+      // the solve does not wait on memory.  The loaded values are not used:
+      // the empty asm only keeps the loads.
+      constexpr int LPT = D / 8, TPW = kWave / LPT, KP = 16;
+      const int sub = lane / LPT, li = lane % LPT;
+      int segs[NW + 1];
+      segs[0] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        segs[w + 1] = segs[w] + __builtin_amdgcn_readfirstlane(s_ccnt[w]);
+      const int n_all = segs[NW];
+      const int h = u % H;
+      for (int e0 = (wave - 1) * TPW + sub; e0 < n_all; e0 += (NW - 1) * TPW * KP) {
+        uint4 x[KP];
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+          const int e = e0 + k * (NW - 1) * TPW;
+          x[k] = make_uint4(0u, 0u, 0u, 0u);
+          if (e < n_all) {
+            int w = 0, base = 0;
+#pragma unroll
+            for (int v = 1; v < NW; ++v)
+              if (e >= segs[v]) { w = v; base = segs[v]; }
+            const int pos = cpos[w * CSEG + (e - base)];
+            const int slot = dslot[pos / P];
+            const char *row = reinterpret_cast<const char *>(
+                vpool + pool_row(slot, h, pos % P, H, P, D));
+            x[k] = *reinterpret_cast<const uint4 *>(row + 16 * li);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < KP; ++k) asm volatile("" ::"v"(x[k].x));
       }
     }
     lds_barrier();
@@ -1101,7 +1152,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
       const int jj = threadIdx.x;
 #pragma unroll
       for (int g = 0; g < G; ++g)
-        act |= pmax[(static_cast<size_t>(u) * G + g) * max_pages + j0 + jj] >
+        act |= pmax[(static_cast<size_t>(u) * G + g) * pm_stride(max_pages) + j0 + jj] >
                tau[u * G + g];
       s_act[jj] = act;
     }

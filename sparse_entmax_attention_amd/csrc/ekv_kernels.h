@@ -36,6 +36,12 @@ inline int max_chunks(const ekv_paged_kv &kv) {
 }
 
 // Decode workspace layout (offsets in bytes, each 256-byte aligned).
+// Row stride of the per-page score maxima in the decode workspace: a
+// multiple of 4 entries, so that rows can be read with 16-byte loads.
+__host__ __device__ inline int pm_stride(int max_pages) {
+  return (max_pages + 3) & ~3;
+}
+
 struct DecodeWs {
   size_t z, cmax, tau, part_o, part_s, ctr, done, slot, total;
 };
