@@ -1815,7 +1815,7 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
   char *w = static_cast<char *>(ws);
   const int units = kv.batch * kv.num_kv_heads;
   const size_t pages = static_cast<size_t>(units) * kv.max_pages;
-  const int blocks = persistent_blocks((pages + kDecWaves - 1) / kDecWaves, 8);
+  const int blocks = persistent_blocks((pages + kDecWaves - 1) / kDecWaves, 4);
   const int cap = kv.max_pages * kv.page_size;
   float *z = reinterpret_cast<float *>(w + L.z);
   float *pm = reinterpret_cast<float *>(w + L.cmax);

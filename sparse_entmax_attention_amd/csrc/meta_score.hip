@@ -120,219 +120,335 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
 
 // ---------------------------------------------------------------------------
 // Page scoring.  Besides the per-page values the kernel writes, for every
-// 64-page tile (one block), summaries the selectors use to skip tiles:
+// 64-page tile, summaries the selectors use to skip tiles:
 //   box:       max over the tile's pages and the group's heads of the bound;
 //   Gaussian:  per query head max mu, max (mu + 8.5 sigma) and
 //              max (mu + sqrt(2 ln P) sigma).
 // They live after the per-page values in the same buffers (see entmaxkv.h).
 //
-// Page scoring: D/8 lanes per page (8 coordinates per lane, 16-byte loads of
-// bf16 box values), 64*8/D pages per wave step.  The box bound uses
-// max(q kmin, q kmax) = q+ kmax + q- kmin per coordinate (q+ = max(q, 0),
-// q- = min(q, 0)): the same rounded product is picked either way.
+// One wave scores one tile of one (sequence, KV head) unit at a time: D/8
+// lanes per page (8 coordinates per lane, see coord_of), 64*8/D pages per
+// step.  The box bound uses max(q kmin, q kmax) = q+ kmax + q- kmin per
+// coordinate (q+ = max(q, 0), q- = min(q, 0)): the same rounded product is
+// picked either way.
+//
+// The metadata loads run kScoreRing steps ahead of the arithmetic: as soon
+// as a step's registers have been used they are refilled with the step
+// kScoreRing further on, past the end of a tile with the first steps of the
+// wave's next tile, so each wave streams its records without a break.  Every
+// load is unconditional (pages past a sequence's end re-read its last page),
+// which keeps the compiler's counts of loads in flight exact; a load behind a
+// branch would make it wait for all of them.  Tiles are numbered over those
+// that hold at least one page (a per-sequence prefix that every block builds
+// in LDS), KV head fastest, and dealt to the waves in turn: the waves running
+// together read every head's record of the same slots, one contiguous
+// stretch of the pool.  The query heads of a wave's next tile are staged
+// through the wave's own LDS rows while the current tile is scored.
 // ---------------------------------------------------------------------------
-constexpr int kScoreTile = kPageTile;  // pages per block
+constexpr int kScoreTile = kPageTile;
+constexpr int kScoreWaves = 4;
+constexpr int kScoreThreads = kScoreWaves * kWave;
+constexpr int kScoreRing = 4;
+// Waves per SIMD the compiler is held to where that costs no spills: one
+// kind of record with up to four query heads per KV head (not float32 boxes
+// with four, whose 32-byte rows need more registers).  Elsewhere it may use
+// the whole register file.
+template <class T, int G, int MODE>
+constexpr int score_min_waves() {
+  if (MODE != EKV_SCORE_BBOX && MODE != EKV_SCORE_GAUSS) return 1;
+  if (G > 4) return 1;
+  if (G == 4 && MODE == EKV_SCORE_BBOX && sizeof(T) == 4) return 1;
+  return 3;
+}
+
+// The 8 coordinates of a row that a lane holds, as loaded (see coord_of).
+template <class T> struct Raw8;
+template <> struct Raw8<float> { float4 a, b; };
+template <> struct Raw8<uint16_t> { uint4 a; };
+
+template <int D>
+__device__ __forceinline__ Raw8<float> load_raw8(const float *row, int li) {
+  Raw8<float> r;
+  r.a = *reinterpret_cast<const float4 *>(row + 4 * li);
+  r.b = *reinterpret_cast<const float4 *>(row + D / 2 + 4 * li);
+  return r;
+}
+template <int D>
+__device__ __forceinline__ Raw8<uint16_t> load_raw8(const uint16_t *row, int li) {
+  Raw8<uint16_t> r;
+  r.a = *reinterpret_cast<const uint4 *>(row + 8 * li);
+  return r;
+}
+__device__ __forceinline__ void unpack8(const Raw8<float> &r, float (&x)[8]) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+__device__ __forceinline__ void unpack8(const Raw8<uint16_t> &r, float (&x)[8]) {
+  x[0] = bf16_lo(r.a.x); x[1] = bf16_hi(r.a.x);
+  x[2] = bf16_lo(r.a.y); x[3] = bf16_hi(r.a.y);
+  x[4] = bf16_lo(r.a.z); x[5] = bf16_hi(r.a.z);
+  x[6] = bf16_lo(r.a.w); x[7] = bf16_hi(r.a.w);
+}
+
+// Max over the lane groups of a wave of a value that is uniform within each
+// group of W lanes.
+template <int W>
+__device__ __forceinline__ float cross_group_max(float x) {
+  if constexpr (W < 16) x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+
+// Keeps a running tile maximum computed at the step that produced it.  The
+// maxima are only read after a tile's last step, and without this the
+// compiler moves every step's update there, holding all the steps' sums in
+// registers at once.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
+// One step's records as loaded: box rows (min, max) and/or Gaussian rows
+// (mean, variance).  Members a mode does not use are never touched.
+template <class T>
+struct ScoreStep {
+  Raw8<T> lo, hi;
+  Raw8<float> mean, var;
+};
+
+struct ScoreItem {
+  int b, h, tile, np;
+};
 
 template <class E, int D, int G, int MODE>
-__global__ __launch_bounds__(256) void k_score(
+__global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, MODE>())) void k_score(
     const typename E::T *__restrict__ bbox, const float *__restrict__ gauss,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const float *__restrict__ q,
     float scale, int H, int P, int max_pages, int batch,
     float *__restrict__ ub, float *__restrict__ gstat) {
-  constexpr int LPP = D / 8;          // lanes per page
-  constexpr int PPW = kWave / LPP;    // pages per wave step
-  constexpr int NWAVE = 4;
-  constexpr int NSTEP = kScoreTile / (NWAVE * PPW);
-  static_assert(kScoreTile % (NWAVE * PPW) == 0, "tile must fill the waves");
+  using T = typename E::T;
+  constexpr bool kBox = (MODE & EKV_SCORE_BBOX) != 0;
+  constexpr bool kGauss = (MODE & EKV_SCORE_GAUSS) != 0;
+  constexpr int LPP = D / 8;               // lanes per page
+  constexpr int PPS = kWave / LPP;         // pages per step
+  constexpr int NSTEP = kScoreTile / PPS;  // steps per tile
+  constexpr int R = kScoreRing;
+  constexpr int QF = G * D / kWave;        // staged query floats per lane
+  static_assert(kScoreTile == kWave, "one page-table entry per lane");
+  static_assert(NSTEP >= R, "the ring must fit in a tile");
+  static_assert(QF == 1 || QF == 2 || QF % 4 == 0, "query staging width");
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int sub = lane / LPP, li = lane % LPP;
   const int Hq = H * G;
   const int n_tiles = (max_pages + kScoreTile - 1) / kScoreTile;
-  const int n_items = batch * H * n_tiles;
-  __shared__ float s_tile[4][3 * G + 1];
 
-  // Persistent blocks over (sequence, KV head, tile) items.  The page-table
-  // entries of a block's next item are read while the current item is
-  // scored, so only the first item waits on them before its metadata loads.
-  auto page_of = [&](int tile, int k) {
-    return tile * kScoreTile + (k * NWAVE + wave) * PPW + sub;
-  };
-  auto fetch_slots = [&](int item, int (&raw)[NSTEP]) {
-    const int b = item / (H * n_tiles);
-    const int tile = item % n_tiles;
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      const int lp = page_of(tile, k);
-      // entries past the sequence end are in bounds (and unused)
-      raw[k] = lp < max_pages ? page_table[static_cast<size_t>(b) * max_pages + lp] : 0;
+  // LDS: per wave G*D staged query floats, then the per-sequence tile prefix
+  // (batch + 1 entries) and page counts (batch entries).
+  extern __shared__ float4 s_dyn4[];
+  float *s_q = reinterpret_cast<float *>(s_dyn4) + wave * G * D;
+  int *s_pref = reinterpret_cast<int *>(s_dyn4) + kScoreWaves * G * D;
+  int *s_np = s_pref + batch + 1;
+  __shared__ int s_tmp[kScoreWaves];
+  {
+    const int per = (batch + kScoreThreads - 1) / kScoreThreads;
+    const int b0 = min(batch, threadIdx.x * per), b1 = min(batch, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) {
+      // pages of sequence b, clamped to its page-table row
+      const int np = max(0, min(n_pages_of(seq_lens[b], P), max_pages));
+      s_np[b] = np;
+      local += (np + kScoreTile - 1) / kScoreTile;
     }
-  };
-  int slot_raw[NSTEP];
-  int item = blockIdx.x;
-  if (item < n_items) fetch_slots(item, slot_raw);
-  for (; item < n_items; item += gridDim.x) {
-    int slot_next[NSTEP];
-    const int nxt = item + gridDim.x;
-    if (nxt < n_items) fetch_slots(nxt, slot_next);
-    const int b = item / (H * n_tiles);
-    const int h = (item / n_tiles) % H;
-    const int tile = item % n_tiles;
-    const int tile0 = tile * kScoreTile;
-    const int len = seq_lens[b];
-    const int np = n_pages_of(len, P);
-    if (tile0 < np) {
-
-  // scale * q at the coordinates this lane owns in a box row (qb) and in a
-  // Gaussian row (qs, float32); see coord_of.
-  float qs[G][8], qb[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float *qg = q + (static_cast<size_t>(b) * Hq + h * G + g) * D;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if constexpr ((MODE & EKV_SCORE_GAUSS) != 0)
-        qs[g][j] = qg[coord_of<float, D>(li, j)] * scale;
-      if constexpr ((MODE & EKV_SCORE_BBOX) != 0)
-        qb[g][j] = qg[coord_of<typename E::T, D>(li, j)] * scale;
+    int total;
+    int base = block_excl_scan<kScoreThreads>(local, s_tmp, total);
+    for (int b = b0; b < b1; ++b) {
+      s_pref[b] = base;
+      base += (s_np[b] + kScoreTile - 1) / kScoreTile;
     }
-  }
-
-  int lps[NSTEP], slots[NSTEP];
-  bool valid[NSTEP];
-#pragma unroll
-  for (int k = 0; k < NSTEP; ++k) {
-    lps[k] = page_of(tile, k);
-    valid[k] = lps[k] < np;
-    slots[k] = valid[k] ? slot_raw[k] : 0;
-  }
-  if constexpr ((MODE & EKV_SCORE_BBOX) != 0) {
-    float tmax = -FLT_MAX;
-    float kmin[NSTEP][8], kmax[NSTEP][8];
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      if (valid[k]) {
-        load8_lane<D>(bbox + meta_row(slots[k], h, 0, H, D), li, kmin[k]);
-        load8_lane<D>(bbox + meta_row(slots[k], h, 1, H, D), li, kmax[k]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { kmin[k][j] = 0.f; kmax[k][j] = 0.f; }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      float acc[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          a = fmaf(fmaxf(qb[g][j], 0.f), kmax[k][j], a);
-          a = fmaf(fminf(qb[g][j], 0.f), kmin[k][j], a);
-        }
-        acc[g] = group_sum<LPP>(a);
-      }
-      if (valid[k]) {
-        float gm = acc[0];
-#pragma unroll
-        for (int g = 1; g < G; ++g) gm = fmaxf(gm, acc[g]);
-        tmax = fmaxf(tmax, gm);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          if (li == g)
-            ub[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lps[k]] = acc[g];
-      }
-    }
-    tmax = group_max<kWave>(tmax);
-    if (lane == 0) s_tile[wave][3 * G] = tmax;
+    if (threadIdx.x == 0) s_pref[batch] = total;
     lds_barrier();
-    if (threadIdx.x == 0) {
-      float m = s_tile[0][3 * G];
-      for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, s_tile[w][3 * G]);
-      ub[static_cast<size_t>(batch) * Hq * max_pages +
-         (static_cast<size_t>(b) * H + h) * n_tiles + tile] = m;
-    }
   }
-  if constexpr ((MODE & EKV_SCORE_GAUSS) != 0) {
-    const float cP = sqrtf(2.0f * logf(static_cast<float>(P)));
+  const int n_items = s_pref[batch] * H;
+  const int n_waves = gridDim.x * kScoreWaves;
+  int it = blockIdx.x * kScoreWaves + wave;
+  if (it >= n_items) return;  // whole waves; no block barrier follows
+
+  int bscan = 0;  // items only move forward, and so does their sequence
+  auto describe = [&](int i) {
+    const int ts = i / H;
+    while (s_pref[bscan + 1] <= ts) ++bscan;
+    ScoreItem d;
+    d.b = __builtin_amdgcn_readfirstlane(bscan);
+    d.h = i - ts * H;
+    d.tile = __builtin_amdgcn_readfirstlane(ts - s_pref[bscan]);
+    d.np = __builtin_amdgcn_readfirstlane(s_np[bscan]);
+    return d;
+  };
+  // Slot of page (tile * 64 + lane), clamped to the sequence's last page.
+  auto load_slots = [&](const ScoreItem &d) {
+    const int lp = min(d.tile * kScoreTile + lane, d.np - 1);
+    return page_table[static_cast<size_t>(d.b) * max_pages + lp];
+  };
+  auto issue = [&](ScoreStep<T> &st, const ScoreItem &d, int slots, int t) {
+    const int slot = __shfl(slots, t * PPS + sub, kWave);
+    if constexpr (kBox) {
+      const T *rb = bbox + meta_row(slot, d.h, 0, H, D);
+      st.lo = load_raw8<D>(rb, li);
+      st.hi = load_raw8<D>(rb + D, li);
+    }
+    if constexpr (kGauss) {
+      const float *rg = gauss + meta_row(slot, d.h, 0, H, D);
+      st.mean = load_raw8<D>(rg, li);
+      st.var = load_raw8<D>(rg + D, li);
+    }
+  };
+  // The G query rows of a unit are contiguous; lane l holds floats
+  // [l QF, (l + 1) QF) of them.
+  auto load_q = [&](const ScoreItem &d, float (&v)[QF]) {
+    const float *src = q + (static_cast<size_t>(d.b) * Hq + d.h * G) * D + lane * QF;
+    if constexpr (QF % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < QF / 4; ++c) {
+        const float4 x = reinterpret_cast<const float4 *>(src)[c];
+        v[4 * c] = x.x; v[4 * c + 1] = x.y; v[4 * c + 2] = x.z; v[4 * c + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < QF; ++j) v[j] = src[j];
+    }
+  };
+  auto stage_q = [&](const float (&v)[QF]) {
+#pragma unroll
+    for (int j = 0; j < QF; ++j) s_q[lane * QF + j] = v[j] * scale;
+  };
+
+  float qv[QF];
+  ScoreItem cur = describe(it);
+  int slots_cur = load_slots(cur);
+  load_q(cur, qv);
+  stage_q(qv);
+  ScoreStep<T> ring[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) issue(ring[t], cur, slots_cur, t);
+  const float cP = sqrtf(2.0f * logf(static_cast<float>(P)));
+  float2 *gpage = reinterpret_cast<float2 *>(gstat);
+  float4 *gtile = reinterpret_cast<float4 *>(gstat + gstat_tile_offset(batch, Hq, max_pages));
+
+  while (true) {
+    const int it_next = it + n_waves;
+    const bool more = it_next < n_items;
+    const ScoreItem nxt = more ? describe(it_next) : cur;
+    const int slots_next = load_slots(nxt);
+    load_q(nxt, qv);
+
+    // this tile's query heads: scale * q at the lane's coordinates
+    float qs[G][8], qp[G][8], qn[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (kGauss) qs[g][j] = s_q[g * D + coord_of<float, D>(li, j)];
+        if constexpr (kBox) {
+          const float x = s_q[g * D + coord_of<T, D>(li, j)];
+          qp[g][j] = fmaxf(x, 0.f);
+          qn[g][j] = fminf(x, 0.f);
+        }
+      }
+    const size_t row0 = (static_cast<size_t>(cur.b) * Hq + cur.h * G) * max_pages;
+    float tmax = -FLT_MAX;
     float t_mu[G], t_pr[G], t_kp[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) { t_mu[g] = -FLT_MAX; t_pr[g] = -FLT_MAX; t_kp[g] = -FLT_MAX; }
-    float mean[NSTEP][8], var[NSTEP][8];
+
 #pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      if (valid[k]) {
-        load8_lane<D>(gauss + meta_row(slots[k], h, 0, H, D), li, mean[k]);
-        load8_lane<D>(gauss + meta_row(slots[k], h, 1, H, D), li, var[k]);
-      } else {
+    for (int s = 0; s < NSTEP; ++s) {
+      ScoreStep<T> &st = ring[s % R];
+      const int lp = cur.tile * kScoreTile + s * PPS + sub;
+      const bool valid = lp < cur.np;
+      if constexpr (kBox) {
+        float kmin[8], kmax[8];
+        unpack8(st.lo, kmin);
+        unpack8(st.hi, kmax);
+        float acc[G];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { mean[k][j] = 0.f; var[k][j] = 0.f; }
-      }
-    }
+        for (int g = 0; g < G; ++g) {
+          float a = 0.f;
 #pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-      float mu[G], s2[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float a = 0.f, c = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = qs[g][j];
-          a = fmaf(x, mean[k][j], a);
-          c = fmaf(x * x, var[k][j], c);
+          for (int j = 0; j < 8; ++j) {
+            a = fmaf(qp[g][j], kmax[j], a);
+            a = fmaf(qn[g][j], kmin[j], a);
+          }
+          acc[g] = group_sum<LPP>(a);
         }
-        mu[g] = group_sum<LPP>(a);
-        s2[g] = group_sum<LPP>(c);
+        float gm = acc[0], mine = acc[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) {
+          gm = fmaxf(gm, acc[g]);
+          mine = li == g ? acc[g] : mine;
+        }
+        tmax = valid ? fmaxf(tmax, gm) : tmax;
+        pin(tmax);
+        if (valid && li < G) ub[row0 + static_cast<size_t>(li) * max_pages + lp] = mine;
       }
-      if (valid[k]) {
+      if constexpr (kGauss) {
+        float mean[8], var[8];
+        unpack8(st.mean, mean);
+        unpack8(st.var, var);
+        float mu[G], s2[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a = 0.f, c = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = qs[g][j];
+            a = fmaf(x, mean[j], a);
+            c = fmaf(x, x * var[j], c);
+          }
+          mu[g] = group_sum<LPP>(a);
+          s2[g] = group_sum<LPP>(c);
+        }
+        float2 mine = make_float2(mu[0], s2[0]);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float sd = sqrtf(fmaxf(s2[g], 0.f));
-          t_mu[g] = fmaxf(t_mu[g], mu[g]);
-          t_pr[g] = fmaxf(t_pr[g], mu[g] + 8.5f * sd);
-          t_kp[g] = fmaxf(t_kp[g], mu[g] + cP * sd);
-          if (li == g) {
-            float2 rr;
-            rr.x = mu[g];
-            rr.y = s2[g];
-            reinterpret_cast<float2 *>(gstat)[(static_cast<size_t>(b) * Hq + h * G + g) * max_pages + lps[k]] = rr;
-          }
+          t_mu[g] = valid ? fmaxf(t_mu[g], mu[g]) : t_mu[g];
+          t_pr[g] = valid ? fmaxf(t_pr[g], mu[g] + 8.5f * sd) : t_pr[g];
+          t_kp[g] = valid ? fmaxf(t_kp[g], mu[g] + cP * sd) : t_kp[g];
+          if (g > 0 && li == g) mine = make_float2(mu[g], s2[g]);
+          pin(t_mu[g]);
+          pin(t_pr[g]);
+          pin(t_kp[g]);
         }
+        if (valid && li < G) gpage[row0 + static_cast<size_t>(li) * max_pages + lp] = mine;
       }
+      // refill: the step R further on, in this tile or the next
+      if (s + R < NSTEP) issue(st, cur, slots_cur, s + R);
+      else issue(st, nxt, slots_next, s + R - NSTEP);
     }
+
+    // tile summaries (every tile holds at least one valid page)
+    if constexpr (kBox) {
+      tmax = cross_group_max<LPP>(tmax);
+      if (lane == 0)
+        ub[static_cast<size_t>(batch) * Hq * max_pages +
+           (static_cast<size_t>(cur.b) * H + cur.h) * n_tiles + cur.tile] = tmax;
+    }
+    if constexpr (kGauss) {
+      float4 mine = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float a0 = group_max<kWave>(t_mu[g]);
-      const float a1 = group_max<kWave>(t_pr[g]);
-      const float a2 = group_max<kWave>(t_kp[g]);
-      if (lane == 0) {
-        s_tile[wave][3 * g] = a0;
-        s_tile[wave][3 * g + 1] = a1;
-        s_tile[wave][3 * g + 2] = a2;
+      for (int g = 0; g < G; ++g) {
+        const float a0 = cross_group_max<LPP>(t_mu[g]);
+        const float a1 = cross_group_max<LPP>(t_pr[g]);
+        const float a2 = cross_group_max<LPP>(t_kp[g]);
+        if (lane == g) mine = make_float4(a0, a1, a2, 0.f);
       }
+      if (lane < G)
+        gtile[(static_cast<size_t>(cur.b) * Hq + cur.h * G + lane) * n_tiles + cur.tile] = mine;
     }
-    lds_barrier();
-    if (threadIdx.x < G) {
-      const int g = threadIdx.x;
-      float4 r4;
-      r4.x = s_tile[0][3 * g];
-      r4.y = s_tile[0][3 * g + 1];
-      r4.z = s_tile[0][3 * g + 2];
-      r4.w = 0.f;
-      for (int w = 1; w < NWAVE; ++w) {
-        r4.x = fmaxf(r4.x, s_tile[w][3 * g]);
-        r4.y = fmaxf(r4.y, s_tile[w][3 * g + 1]);
-        r4.z = fmaxf(r4.z, s_tile[w][3 * g + 2]);
-      }
-      float4 *gt = reinterpret_cast<float4 *>(
-          gstat + gstat_tile_offset(batch, Hq, max_pages));
-      gt[(static_cast<size_t>(b) * Hq + h * G + g) * n_tiles + tile] = r4;
-    }
-  }
-    }
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) slot_raw[k] = slot_next[k];
-    lds_barrier();  // s_tile is rewritten by the next item
+    if (!more) break;
+    // this tile's query reads are done (their values are in registers)
+    stage_q(qv);
+    cur = nxt;
+    slots_cur = slots_next;
+    it = it_next;
   }
 }
 
@@ -353,12 +469,16 @@ hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
   return hipGetLastError();
 }
 
+// Waves stay resident and walk their tiles; the grid is as many blocks as fit
+// on the device at once (fewer if there are fewer tiles than waves).
 template <class E, int D, int G>
 hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
                         const float *q, float scale, int mode, float *ub,
                         float *gstat, hipStream_t stream) {
-  const int items = ((kv.max_pages + kScoreTile - 1) / kScoreTile) *
-                    kv.num_kv_heads * kv.batch;
+  const long long items = static_cast<long long>(page_tiles(kv)) *
+                          kv.num_kv_heads * kv.batch;
+  const size_t lds = static_cast<size_t>(kScoreWaves) * G * D * sizeof(float) +
+                     (2 * static_cast<size_t>(kv.batch) + 1) * sizeof(int);
   auto launch = [&](auto kern) {
     int dev = 0, n_cu = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -366,11 +486,13 @@ hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
             hipSuccess || n_cu <= 0)
       n_cu = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(kern), 256, 0) != hipSuccess ||
-        per_cu <= 0)
+            &per_cu, reinterpret_cast<const void *>(kern), kScoreThreads, lds) !=
+            hipSuccess || per_cu <= 0)
       per_cu = 1;
-    const int blocks = std::min(items, n_cu * per_cu);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream,
+    const long long want = (items + kScoreWaves - 1) / kScoreWaves;
+    const int blocks = static_cast<int>(
+        std::min<long long>(want, static_cast<long long>(n_cu) * per_cu));
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kScoreThreads), lds, stream,
                        static_cast<const typename E::T *>(meta.bbox),
                        meta.gauss, kv.page_table, kv.seq_lens, q, scale,
                        kv.num_kv_heads, kv.page_size, kv.max_pages, kv.batch,
