@@ -82,8 +82,10 @@ typedef enum ekv_dtype {
  *   page_table  [batch][max_pages] int32 logical page -> slot
  *   seq_lens    [batch] int32 valid tokens of each sequence
  * Supported: head_dim in {64, 128}; page_size in {16, 32, 64};
- * group in {1, 2, 4, 8}; kv_dtype EKV_F32 or EKV_BF16.  k, v and the
- * metadata arrays must be 16-byte aligned.
+ * group in {1, 2, 4, 8}; kv_dtype EKV_F32 or EKV_BF16; batch *
+ * num_kv_heads <= 4096; group * max_pages * page_size * 4 bytes (one unit's
+ * scores) below 2 GiB - 64 KiB.  k, v and the metadata arrays must be
+ * 16-byte aligned.
  */
 typedef struct ekv_paged_kv {
   int32_t batch;

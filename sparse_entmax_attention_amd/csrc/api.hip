@@ -58,9 +58,13 @@ ekv_status check_kv(const ekv_paged_kv *kv, bool need_k, bool need_v) {
                 kv->group);
   if (static_cast<long long>(kv->batch) * kv->num_kv_heads > 4096)
     return fail(EKV_ERR_UNSUPPORTED, "batch * num_kv_heads exceeds 4096");
-  const double cells = static_cast<double>(kv->max_pages) * kv->page_size;
-  if (cells > 2147483647.0)
-    return fail(EKV_ERR_UNSUPPORTED, "max_pages * page_size exceeds 2^31-1");
+  // one unit's float32 scores must be addressable by a 32-bit byte offset
+  // of a buffer store (kernels write them through range-checked stores)
+  const double unit_bytes =
+      static_cast<double>(kv->max_pages) * kv->page_size * kv->group * 4.0;
+  if (unit_bytes > 2147418112.0)
+    return fail(EKV_ERR_UNSUPPORTED,
+                "group * max_pages * page_size * 4 bytes exceeds 2 GiB - 64 KiB");
   if (!kv->page_table || !kv->seq_lens)
     return fail(EKV_ERR_INVALID_ARG, "page_table and seq_lens are required");
   if (need_k && (!kv->k || !aligned(kv->k, 16)))

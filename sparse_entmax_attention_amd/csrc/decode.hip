@@ -17,6 +17,8 @@
 // HBM reads: selected K once, V only on the support, z twice.
 #include <float.h>
 
+#include <type_traits>
+
 #include "ekv_device.h"
 #include "ekv_kernels.h"
 
@@ -43,7 +45,7 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   w.part_o = al(w.tau + units * G * 4);
   w.part_s = al(w.part_o + units * mc * G * D * 4);
   w.ctr = al(w.part_s + units * mc * G * 4);  // chunks finished, per unit
-  w.done = al(w.ctr + units * 4);
+  w.done = al(w.ctr + (units + 1) * 4);  // + heads left to the apply step
   w.slot = al(w.done + units * G * 4);  // pool slot per selected page
   w.total = al(w.slot + units * static_cast<size_t>(kv.max_pages) * 4);
   return w;
@@ -189,17 +191,34 @@ __device__ __forceinline__ void load_q_parts(bf16x8_t (&a)[(G + 3) / 4][D / 32],
   }
 }
 
-template <int D, int G, int P>
+// Each wave takes a contiguous run of the flattened list of selected pages
+// (units in order, so a run seldom crosses into another unit) and walks it in
+// chunks of up to 64 pages.  A chunk's page references are loaded first, one
+// page per lane (selection entry, sequence length, then page-table entry),
+// and read back with readlane; its keys then stream in bodies of kKRing
+// 16-token groups (one page of 64 tokens, two of 32 or four of 16).  As soon
+// as a group has been used its registers are refilled with the same group of
+// the next body, so one body of keys is always in flight.  Every load in the
+// stream is unconditional (the refill after a chunk's last body repeats that
+// body and is never used), so the compiler's counts of loads in flight stay
+// exact and the wait for one group never waits for the groups behind it.
+constexpr int kKRing = 4;
+
+template <int D, int G, int P, bool SEL>
 __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
     const uint16_t *__restrict__ kpool, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
     float zscale, int units, int H, int max_pages, int cap,
     float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots) {
+    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
   constexpr int KS = D / 32;            // k-steps of 32 coordinates
   constexpr int NPASS = (G + 3) / 4;    // groups of 4 query heads
   constexpr int NT16 = P / 16;          // 16-token groups per page
+  constexpr int U = kKRing / NT16;      // pages per body
+  // the threshold step counts the heads it leaves to the apply step
+  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
+  static_assert(kKRing % NT16 == 0, "a body holds whole pages");
   __shared__ int pref[kMaxUnits + 1];
   __shared__ int tmp[kDecWaves];
   const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
@@ -207,77 +226,115 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, kb = lane >> 4;
   const int nwaves = gridDim.x * kDecWaves;
+  const int wg = blockIdx.x * kDecWaves + wave;
+  const int per = ((total + U - 1) / U + nwaves - 1) / nwaves;  // bodies
+  const int f0 = wg * per * U;
+  const int f1 = min(total, f0 + per * U);
+  if (f0 >= f1) return;  // whole waves; no block barrier follows
+
+  auto issue = [&](bf16x8_t (&bv)[KS], int slot, int h, int t) {
+    const uint16_t *row = kpool + pool_row(slot, h, 16 * t + n, H, P, D) + 8 * kb;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      bv[s] = *reinterpret_cast<const bf16x8_t *>(row + 32 * s);
+  };
+  auto lane_val = [](int x, int i) { return __builtin_amdgcn_readlane(x, i); };
 
   bf16x8_t a[NPASS][KS];
+  bf16x8_t ring[kKRing][KS];
   int cur_u = -1;
-  int f = blockIdx.x * kDecWaves + wave;
-  if (f >= total) return;
-  PageRef cur = page_ref(pref, units, f, page_table, seq_lens, sel, H, P,
-                         max_pages);
-  while (true) {
-    const int fn = f + nwaves;
-    PageRef nxt = cur;
-    if (fn < total)
-      nxt = page_ref(pref, units, fn, page_table, seq_lens, sel, H, P,
-                     max_pages);
-    const int u = cur.u, h = u % H, b = u / H;
-    if (u != cur_u) {
-      cur_u = u;
-      load_q_parts<D, G>(a, q, b, h, H, zscale);
+  for (int c0 = f0; c0 < f1; c0 += kWave) {
+    const int nc = min(kWave, f1 - c0);        // pages in this chunk
+    const int nbc = (nc + U - 1) / U;          // bodies in this chunk
+    // page references, one page per lane (lanes past the chunk repeat its last)
+    const int f = c0 + min(lane, nc - 1);
+    const int ru = find_unit(pref, units, f);
+    const int rj = f - pref[ru];
+    const int rb = ru / H;
+    int rlp;
+    if constexpr (SEL) rlp = sel[static_cast<size_t>(ru) * max_pages + rj];
+    else rlp = rj;
+    const int rnt = page_tokens(rlp, seq_lens[rb], P);
+    const int rslot = page_table[static_cast<size_t>(rb) * max_pages + rlp];
+    auto body_page = [&](int k, int t) { return min(k * U + t, nc - 1); };
+#pragma unroll
+    for (int s = 0; s < kKRing; ++s) {
+      const int i = body_page(0, s / NT16);
+      issue(ring[s], lane_val(rslot, i), lane_val(ru, i) % H, s % NT16);
     }
-    const uint16_t *base = kpool + pool_row(cur.slot, h, 0, H, P, D);
-    bf16x8_t bv[NT16][KS];
+    for (int k = 0; k < nbc; ++k) {
+      float pm[NPASS][4];
 #pragma unroll
-    for (int t = 0; t < NT16; ++t)
+      for (int s = 0; s < kKRing; ++s) {
+        const int t = s / NT16, tt = s % NT16;
+        const int i = k * U + t;               // page of the chunk
+        const bool live = i < nc;
+        const int ic = min(i, nc - 1);
+        const int u = lane_val(ru, ic);
+        const int j = lane_val(rj, ic);
+        const int h = u % H;
+        if (tt == 0) {
+          if (u != cur_u) {  // rare: the run enters another unit
+            cur_u = u;
+            load_q_parts<D, G>(a, q, u / H, h, H, zscale);
+          }
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        bv[t][s] = *reinterpret_cast<const bf16x8_t *>(
-            base + static_cast<size_t>(16 * t + n) * D + 32 * s + 8 * kb);
-    float *zu = zbuf + static_cast<size_t>(u) * G * cap +
-                static_cast<size_t>(cur.j) * P;
-    float pm[NPASS][4];
+          for (int ps = 0; ps < NPASS; ++ps)
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps)
+            for (int e = 0; e < 4; ++e) pm[ps][e] = -FLT_MAX;
+        }
+        const bool valid = 16 * tt + n < lane_val(rnt, ic);
+        const __amdgpu_buffer_rsrc_t zr = store_rsrc(
+            zbuf + static_cast<size_t>(u) * G * cap,
+            static_cast<size_t>(G) * cap * sizeof(float));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pm[ps][i] = -FLT_MAX;
+        for (int ps = 0; ps < NPASS; ++ps) {
+          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < NT16; ++t) {
-      const bool valid = 16 * t + n < cur.nt;
+          for (int s2 = 0; s2 < KS; ++s2)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s2], ring[s][s2], c,
+                                                        0, 0, 0);
 #pragma unroll
-      for (int ps = 0; ps < NPASS; ++ps) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], bv[t][s], c,
-                                                      0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p1 = __shfl_down(c[i], 16, kWave);
-          const float p2 = __shfl_down(c[i], 32, kWave);
-          const float z = c[i] + (p1 + p2);
-          const int g = 4 * ps + i;
-          if (g < G && lane < 16) {
-            zu[static_cast<size_t>(g) * cap + 16 * t + n] = valid ? z : -INFINITY;
-            if (valid) pm[ps][i] = fmaxf(pm[ps][i], z);
+          for (int e = 0; e < 4; ++e) {
+            const float p1 = __shfl_down(c[e], 16, kWave);
+            const float p2 = __shfl_down(c[e], 32, kWave);
+            const float z = c[e] + (p1 + p2);
+            const int g = 4 * ps + e;
+            if (g < G)
+              store_if(zr, 4 * (g * cap + j * P + 16 * tt + n), lane < 16 && live,
+                       valid ? z : -INFINITY);
+            if (valid) pm[ps][e] = fmaxf(pm[ps][e], z);
           }
         }
+        if (tt == NT16 - 1) {
+          // the page's maxima, lane g holding head g's
+          float mine = 0.f;
+#pragma unroll
+          for (int ps = 0; ps < NPASS; ++ps)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int g = 4 * ps + e;
+              if (g < G) {
+                const float m = group_max<16>(pm[ps][e]);
+                const float m0 = __shfl(m, 0, kWave);
+                mine = lane == g ? m0 : mine;
+              }
+            }
+          const int ps_ = pm_stride(max_pages);
+          const __amdgpu_buffer_rsrc_t pr = store_rsrc(
+              pmax + static_cast<size_t>(u) * G * ps_,
+              static_cast<size_t>(G) * ps_ * sizeof(float));
+          store_if(pr, 4 * (lane * ps_ + j), lane < G && live, mine);
+          const __amdgpu_buffer_rsrc_t sr = store_rsrc(
+              slots + static_cast<size_t>(u) * max_pages,
+              static_cast<size_t>(max_pages) * sizeof(int32_t));
+          store_if(sr, 4 * j, lane == 0 && live, lane_val(rslot, ic));
+        }
+        // refill: the same group of the next body
+        const int inx = body_page(k + 1, t);
+        issue(ring[s], lane_val(rslot, inx), lane_val(ru, inx) % H, tt);
       }
     }
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int g = 4 * ps + i;
-        if (g < G) {
-          const float m = group_max<16>(pm[ps][i]);
-          if (lane == 0)
-            pmax[(static_cast<size_t>(u) * G + g) * pm_stride(max_pages) + cur.j] = m;
-        }
-      }
-    if (lane == 0) slots[static_cast<size_t>(u) * max_pages + cur.j] = cur.slot;
-    if (fn >= total) break;
-    f = fn;
-    cur = nxt;
   }
 }
 
@@ -293,7 +350,8 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
     const int32_t *__restrict__ count, const float *__restrict__ q,
     float zscale, int units, int H, int P, int max_pages, int cap,
     float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots) {
+    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   __shared__ int pref[kMaxUnits + 1];
@@ -369,6 +427,37 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
 // the order the block visits the tokens.  General alpha, or a bracket with
 // too many undecided tokens, falls back to bisection in double.
 // ---------------------------------------------------------------------------
+// One pass of the support iteration reduces four values over a wave: the
+// count, the sums of y and y^2, and the minimum.  The four are taken through
+// each swizzle level together, so their dependency chains overlap, and the
+// result (lane 63 after the row broadcasts) is read back to every lane.
+__device__ __forceinline__ void wave_reduce_pass(int &k, double &sy, double &sy2,
+                                                 float &zmin) {
+#define EKV_PASS_LEVEL(CTRL)                            \
+  k += dpp_i<CTRL>(k);                                  \
+  sy += dpp_d<CTRL>(sy);                                \
+  sy2 += dpp_d<CTRL>(sy2);                              \
+  zmin = fminf(zmin, dpp_f<CTRL>(zmin));
+  EKV_PASS_LEVEL(kDppRowMirror)
+  EKV_PASS_LEVEL(kDppRowHalfMirror)
+  EKV_PASS_LEVEL(kDppQuad2301)
+  EKV_PASS_LEVEL(kDppQuad1032)
+#undef EKV_PASS_LEVEL
+  const int idle = __float_as_int(FLT_MAX);
+  k += dpp_rows<kDppRowBcast15, 0xA>(k, 0);
+  sy += dpp_rows_d<kDppRowBcast15, 0xA>(sy);
+  sy2 += dpp_rows_d<kDppRowBcast15, 0xA>(sy2);
+  zmin = fminf(zmin, __int_as_float(dpp_rows<kDppRowBcast15, 0xA>(__float_as_int(zmin), idle)));
+  k += dpp_rows<kDppRowBcast31, 0xC>(k, 0);
+  sy += dpp_rows_d<kDppRowBcast31, 0xC>(sy);
+  sy2 += dpp_rows_d<kDppRowBcast31, 0xC>(sy2);
+  zmin = fminf(zmin, __int_as_float(dpp_rows<kDppRowBcast31, 0xC>(__float_as_int(zmin), idle)));
+  k = __builtin_amdgcn_readlane(k, kWave - 1);
+  sy = readlane_d(sy, kWave - 1);
+  sy2 = readlane_d(sy2, kWave - 1);
+  zmin = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zmin), kWave - 1));
+}
+
 constexpr int kTauThreads = 512;
 constexpr int kTauBins = 2048;
 constexpr int kTauList = 1024;
@@ -462,7 +551,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     int cap, int r, float rg, float *__restrict__ tau_ws,
     float *__restrict__ tau_user, float *__restrict__ out,
     int32_t *__restrict__ done, int32_t *__restrict__ ctr,
-    const int32_t *__restrict__ slots) {
+    const int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
   constexpr int NW = kTauThreads / kWave;
   constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
   constexpr int CSEG = kTauCandCap / NW;  // staged candidates per wave
@@ -488,6 +577,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   __shared__ double s_wtau;
 
   const int ug = blockIdx.x, u = ug / G;
+  const int lgP = __builtin_ctz(P);  // page sizes are powers of two
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int mps = pm_stride(max_pages);
   const float *zh = zbuf + static_cast<size_t>(ug) * cap;
@@ -669,6 +759,21 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   double blo = L, bhi = Md;  // bracket for the fallback
 
   // Exact solve by support iteration (r in {1, 2}, candidates staged), by
+  // the whole block.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
+  // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
+  // over S(t) = {y > t}, the count K, sum y and sum y^2, and finds min_S y.
+  // The closed form t* of tau for the support S (sparsemax: (sum y - 1)/K;
+  // 1.5-entmax: the smaller root of sum_S (y - t)^2 = 1) is tau itself when
+  // t* < min_S y, since then S(t*) = S.  Otherwise t moves up: for r = 1 to
+  // t* (over a superset of the support the terms below tau are negative, so
+  // t* <= tau: Michelot's iteration), for r = 2 by a Newton step on
+  // F^(1/2) - 1 (convex, so the step stays below tau).  Each wave reduces
+  // its threads' sums in a fixed pattern and the wave totals are added in
+  // wave order, so every thread takes the same steps and the result is the
+  // same on every run.  One barrier per pass; the wave totals alternate
+  // between two LDS rows so that a pass never overwrites totals still being
+  // read.
+  // Exact solve by support iteration (r in {1, 2}, candidates staged), by
   // wave 0 alone.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
   // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
   // over S(t) = {y > t}, the count K, sum y and sum y^2, and finds min_S y.
@@ -729,10 +834,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
           for (int w = 0; w < NW; ++w)
             for (int i = lane; i < s_ccnt[w]; i += kWave) visit(cand[w * CSEG + i]);
         }
-        K = group_sum_i<kWave>(K);
-        SY = group_sum_d<kWave>(SY);
-        SY2 = group_sum_d<kWave>(SY2);
-        zmin = -group_max<kWave>(-zmin);
+        wave_reduce_pass(K, SY, SY2, zmin);
         if (K == 0) break;
         const double kd = static_cast<double>(K);
         const double ymin = static_cast<double>(zmin) - Md;
@@ -787,9 +889,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
             for (int v = 1; v < NW; ++v)
               if (e >= segs[v]) { w = v; base = segs[v]; }
             const int pos = cpos[w * CSEG + (e - base)];
-            const int slot = dslot[pos / P];
+            const int slot = dslot[pos >> lgP];
             const char *row = reinterpret_cast<const char *>(
-                vpool + pool_row(slot, h, pos % P, H, P, D));
+                vpool + pool_row(slot, h, pos & (P - 1), H, P, D));
             x[k] = *reinterpret_cast<const uint4 *>(row + 16 * li);
           }
         }
@@ -945,7 +1047,10 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   // reset here for it.
   if (tid == 0 && ug % G == 0) ctr[u] = 0;
   if (!staged) {
-    if (tid == 0) done[ug] = 0;
+    if (tid == 0) {
+      done[ug] = 0;
+      atomicAdd(undone, 1);
+    }
     return;
   }
   constexpr int LPT = D / 8, TPW = kWave / LPT, RU = 8;
@@ -988,7 +1093,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       if (k < nk) {
         pw[rr] = cand[wave * CSEG + k];
         const int pos = cpos[wave * CSEG + k];
-        const int jj = pos / P, t = pos - jj * P;
+        const int jj = pos >> lgP, t = pos & (P - 1);
         const int slot =
             listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
         load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
@@ -1116,10 +1221,13 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_apply(
     const float *__restrict__ pmax, const float *__restrict__ tau,
     float *__restrict__ part_o, float *__restrict__ part_s,
     float *__restrict__ probs, const int32_t *__restrict__ done,
-    int32_t *__restrict__ ctr, float *__restrict__ out) {
+    int32_t *__restrict__ ctr, const int32_t *__restrict__ undone,
+    float *__restrict__ out) {
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   constexpr int ROWS_STEP = kDecWaves * TPW * kRowUnroll;
+  // Nothing to do when the threshold step finished every head.
+  if (done && *undone == 0) return;
   __shared__ int pref[kMaxUnits + 1];
   __shared__ int tmp[kDecWaves];
   __shared__ ChunkPages cp;
@@ -1806,6 +1914,23 @@ static int persistent_blocks(size_t max_items, int per_cu) {
   return static_cast<int>(max_items < cap ? max_items : cap);
 }
 
+// Blocks of `kern` the device holds at once, at most `max_items`.
+template <class K>
+static int resident_blocks(K kern, int threads, size_t max_items) {
+  int dev = 0, n_cu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount,
+                            dev) != hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void *>(kern), threads, 0) !=
+          hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const size_t cap = static_cast<size_t>(n_cu) * per_cu;
+  if (max_items == 0) return 1;
+  return static_cast<int>(max_items < cap ? max_items : cap);
+}
+
 template <class E, int D, int G>
 hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 float scale, float alpha, const int32_t *sel,
@@ -1820,35 +1945,34 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
   float *z = reinterpret_cast<float *>(w + L.z);
   float *pm = reinterpret_cast<float *>(w + L.cmax);
   int32_t *sl = reinterpret_cast<int32_t *>(w + L.slot);
+  int32_t *und = reinterpret_cast<int32_t *>(w + L.ctr) + units;
   const float zs = (alpha - 1.0f) * scale;
   if constexpr (sizeof(typename E::T) == 2) {
     const uint16_t *k = static_cast<const uint16_t *>(kv.k);
-    switch (kv.page_size) {
-      case 16:
-        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 16>), dim3(blocks),
-                           dim3(kDecThreads), 0, stream, k, kv.page_table,
-                           kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
-        break;
-      case 32:
-        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 32>), dim3(blocks),
-                           dim3(kDecThreads), 0, stream, k, kv.page_table,
-                           kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
-        break;
-      default:
-        hipLaunchKernelGGL((k_entmax_scores_mfma<D, G, 64>), dim3(blocks),
-                           dim3(kDecThreads), 0, stream, k, kv.page_table,
-                           kv.seq_lens, sel, count, q, zs, units,
-                           kv.num_kv_heads, kv.max_pages, cap, z, pm, sl);
-        break;
-    }
+    // resident waves walk contiguous runs of pages
+    auto go = [&](auto kern) {
+      const int nb = resident_blocks(kern, kDecThreads,
+                                     (pages + kDecWaves - 1) / kDecWaves);
+      hipLaunchKernelGGL(kern, dim3(nb), dim3(kDecThreads), 0, stream, k,
+                         kv.page_table, kv.seq_lens, sel, count, q, zs, units,
+                         kv.num_kv_heads, kv.max_pages, cap, z, pm, sl, und);
+    };
+    auto by_page = [&](auto has_sel) {
+      constexpr bool S = decltype(has_sel)::value;
+      switch (kv.page_size) {
+        case 16: go(k_entmax_scores_mfma<D, G, 16, S>); break;
+        case 32: go(k_entmax_scores_mfma<D, G, 32, S>); break;
+        default: go(k_entmax_scores_mfma<D, G, 64, S>); break;
+      }
+    };
+    if (sel) by_page(std::true_type());
+    else by_page(std::false_type());
   } else {
     hipLaunchKernelGGL((k_entmax_scores_valu<E, D, G>), dim3(blocks),
                        dim3(kDecThreads), 0, stream,
                        static_cast<const typename E::T *>(kv.k), kv.page_table,
                        kv.seq_lens, sel, count, q, zs, units, kv.num_kv_heads,
-                       kv.page_size, kv.max_pages, cap, z, pm, sl);
+                       kv.page_size, kv.max_pages, cap, z, pm, sl, und);
   }
   return hipGetLastError();
 }
@@ -1872,7 +1996,8 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<float *>(w + L.tau), tau, out,
                      reinterpret_cast<int32_t *>(w + L.done),
                      reinterpret_cast<int32_t *>(w + L.ctr),
-                     reinterpret_cast<const int32_t *>(w + L.slot));
+                     reinterpret_cast<const int32_t *>(w + L.slot),
+                     reinterpret_cast<int32_t *>(w + L.ctr) + kv.batch * kv.num_kv_heads);
   return hipGetLastError();
 }
 
@@ -1909,7 +2034,8 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                      reinterpret_cast<const float *>(w + L.tau),
                      reinterpret_cast<float *>(w + L.part_o),
                      reinterpret_cast<float *>(w + L.part_s), probs, done,
-                     reinterpret_cast<int32_t *>(w + L.ctr), out);
+                     reinterpret_cast<int32_t *>(w + L.ctr),
+                     reinterpret_cast<const int32_t *>(w + L.ctr) + units, out);
   return hipGetLastError();
 }
 

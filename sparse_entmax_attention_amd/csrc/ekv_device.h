@@ -1,6 +1,7 @@
 // Device-side helpers shared by the EntmaxKV HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <float.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -158,6 +159,54 @@ __device__ __forceinline__ int group_sum_i(int x) {
   return x;
 }
 
+// Whole-wave reductions with the result in every lane.  Each 16-lane row is
+// reduced with the swizzles above; then row_bcast:15 carries the last lane
+// of rows 0 and 2 into rows 1 and 3, and row_bcast:31 carries lane 31 into
+// rows 2 and 3, which leaves the total in lane 63 (read back to all lanes).
+// No lane exchange goes through LDS, and the summation order is fixed.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows(int x, int idle) {
+  return __builtin_amdgcn_update_dpp(idle, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const unsigned long long v = static_cast<unsigned long long>(__double_as_longlong(x));
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(v), l);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(v >> 32), l);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(hi) << 32) | lo));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_rows_d(double x) {  // idle rows read 0.0
+  const unsigned long long v = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = dpp_rows<CTRL, ROWS>(static_cast<int>(v), 0);
+  const int hi = dpp_rows<CTRL, ROWS>(static_cast<int>(v >> 32), 0);
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(static_cast<unsigned int>(hi)) << 32) |
+      static_cast<unsigned int>(lo)));
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x = group_sum_d<16>(x);
+  x += dpp_rows_d<kDppRowBcast15, 0xA>(x);
+  x += dpp_rows_d<kDppRowBcast31, 0xC>(x);
+  return readlane_d(x, kWave - 1);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x = group_sum_i<16>(x);
+  x += dpp_rows<kDppRowBcast15, 0xA>(x, 0);
+  x += dpp_rows<kDppRowBcast31, 0xC>(x, 0);
+  return __builtin_amdgcn_readlane(x, kWave - 1);
+}
+__device__ __forceinline__ float wave_min_f(float x) {
+  x = -group_max<16>(-x);
+  const int idle = __float_as_int(FLT_MAX);
+  x = fminf(x, __int_as_float(dpp_rows<kDppRowBcast15, 0xA>(__float_as_int(x), idle)));
+  x = fminf(x, __int_as_float(dpp_rows<kDppRowBcast31, 0xC>(__float_as_int(x), idle)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+
 // Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
 // it does not wait for outstanding global loads, so loads issued before it
 // stay in flight.  Use it wherever threads exchange data through LDS alone.
@@ -262,6 +311,35 @@ __device__ __forceinline__ int tile_rank(bool flag, int *smem, int &total) {
   }
   total = tot;
   return base + below;
+}
+
+// ---------------------------------------------------------------------------
+// Range-checked buffer stores.  A raw buffer resource covers `bytes` bytes
+// from a wave-uniform base, and the hardware drops a lane's store when the
+// lane's byte offset lies past the end.  Streaming kernels use them for
+// stores that only some lanes make: behind a branch, a store would make the
+// compiler assume it may not have been issued and then wait for more of the
+// loads in flight than it needs to.
+// ---------------------------------------------------------------------------
+constexpr int kDropOffset = 0x7fffffff;  // past the end of every resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(void *base,
+                                                             size_t bytes) {
+  // word 3: 32-bit data format, no swizzle; sizes are capped below the
+  // drop offset
+  const int n = static_cast<int>(bytes < 0x7fff0000u ? bytes : 0x7fff0000u);
+  return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), n,
+                                           0x00020000);
+}
+__device__ __forceinline__ void store_if(__amdgpu_buffer_rsrc_t r, int byte_off,
+                                         bool on, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r,
+                                        on ? byte_off : kDropOffset, 0, 0);
+}
+__device__ __forceinline__ void store_if(__amdgpu_buffer_rsrc_t r, int byte_off,
+                                         bool on, int v) {
+  __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(v), r,
+                                        on ? byte_off : kDropOffset, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -91,6 +91,8 @@ def test_validation_errors(lib):
     assert _topk(lib, _kv(head_dim=96)) == B.EKV_ERR_UNSUPPORTED
     assert _topk(lib, _kv(page_size=8)) == B.EKV_ERR_UNSUPPORTED
     assert _topk(lib, _kv(group=3)) == B.EKV_ERR_UNSUPPORTED
+    # one unit's float32 scores past 2 GiB - 64 KiB
+    assert _topk(lib, _kv(group=8, page_size=64, max_pages=1 << 20)) == B.EKV_ERR_UNSUPPORTED
     assert _topk(lib, _kv(kv_dtype=7)) == B.EKV_ERR_INVALID_ARG
     assert _topk(lib, _kv(page_table=None)) == B.EKV_ERR_INVALID_ARG
     assert _topk(lib, _kv(), ws=None) == B.EKV_ERR_WORKSPACE
