@@ -89,7 +89,7 @@ class DeviceEvents:
 
 
 TRAFFIC_FILE = os.path.join(REPO, "profiles", "hbm_traffic_cluster_1m.txt")
-KERNEL_SOURCES = ("decode.hip", "ekv_device.h", "ekv_kernels.h")
+KERNEL_SOURCES = ("kpass.hip", "decode_common.h", "ekv_device.h", "ekv_kernels.h")
 
 
 def kernel_source_hash():

@@ -4,9 +4,10 @@
 //
 // Entmax has no single-pass running form: the threshold tau depends on every
 // score.  The step is therefore split in three launches:
-//   1. scores:    one wave per selected page gathers its keys and computes
-//                 z = (alpha-1) scale <q, k> for the G query heads on the
-//                 matrix cores; z and each page's maximum are written;
+//   1. scores:    (kpass.hip) the selected pages' keys are gathered and
+//                 z = (alpha-1) scale <q, k> is computed for the G query
+//                 heads on the matrix cores; z and each page's maximum are
+//                 written;
 //   2. threshold: per query head, tau from the tokens that can still be in
 //                 the support (tau is at least max z - 1, and at least
 //                 c - k^-(alpha-1) whenever k page maxima reach c); exact
@@ -17,20 +18,9 @@
 // HBM reads: selected K once, V only on the support, z twice.
 #include <float.h>
 
-#include <type_traits>
-
-#include "ekv_device.h"
-#include "ekv_kernels.h"
+#include "decode_common.h"
 
 namespace ekv {
-
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kMaxChunkPages = kChunkTokens / 16;  // smallest page size
-constexpr int kMaxUnits = 4096;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   const size_t units = static_cast<size_t>(kv.batch) * kv.num_kv_heads;
@@ -62,343 +52,6 @@ SoftmaxWs softmax_ws_layout(const ekv_paged_kv &kv) {
   w.part_o = al(w.part_l + units * mc * G * 4);
   w.total = al(w.part_o + units * mc * G * D * 4);
   return w;
-}
-
-// ---------------------------------------------------------------------------
-// Work lists.  Work items (pages or chunks of pages) of all units are laid
-// end to end, unit by unit; a persistent grid walks them with a stride.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int unit_pages(const int32_t *seq_lens,
-                                          const int32_t *sel,
-                                          const int32_t *count, int u, int H,
-                                          int P) {
-  return sel ? count[u] : n_pages_of(seq_lens[u / H], P);
-}
-
-// pref[u] = first item of unit u (pref[units] = total); returns the total.
-// With `done` (one flag per query head, G per unit), units whose heads are
-// all done contribute no items.
-template <int NT>
-__device__ int build_unit_prefix(int *pref, int *tmp, const int32_t *seq_lens,
-                                 const int32_t *sel, const int32_t *count,
-                                 int units, int H, int P, int pages_per_item,
-                                 const int32_t *done = nullptr, int G = 0) {
-  const int per = (units + NT - 1) / NT;
-  const int u0 = threadIdx.x * per, u1 = min(units, u0 + per);
-  auto items = [&](int u) {
-    if (done) {
-      bool all = true;
-      for (int g = 0; g < G; ++g) all &= done[u * G + g] != 0;
-      if (all) return 0;
-    }
-    return (unit_pages(seq_lens, sel, count, u, H, P) + pages_per_item - 1) /
-           pages_per_item;
-  };
-  int local = 0;
-  for (int u = u0; u < u1; ++u) local += items(u);
-  int total;
-  int base = block_excl_scan<NT>(local, tmp, total);
-  for (int u = u0; u < u1; ++u) {
-    pref[u] = base;
-    base += items(u);
-  }
-  if (threadIdx.x == 0) pref[units] = total;
-  lds_barrier();
-  return total;
-}
-
-// Largest u with pref[u] <= f.
-__device__ __forceinline__ int find_unit(const int *pref, int units, int f) {
-  int lo = 0, hi = units - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pref[mid] <= f) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Location of a selected page.
-struct PageRef {
-  int u, j, lp, slot, nt;
-};
-
-__device__ __forceinline__ PageRef page_ref(const int *pref, int units, int f,
-                                            const int32_t *page_table,
-                                            const int32_t *seq_lens,
-                                            const int32_t *sel, int H, int P,
-                                            int max_pages) {
-  PageRef r;
-  r.u = find_unit(pref, units, f);
-  r.j = f - pref[r.u];
-  const int b = r.u / H;
-  r.lp = sel ? sel[static_cast<size_t>(r.u) * max_pages + r.j] : r.j;
-  r.slot = page_table[static_cast<size_t>(b) * max_pages + r.lp];
-  r.nt = page_tokens(r.lp, seq_lens[b], P);
-  return r;
-}
-
-__device__ __forceinline__ float pow_r(float x, int r, float rg) {
-  // x >= 0.  r = 1 (alpha = 2), r = 2 (alpha = 1.5), else x^rg.
-  if (r == 1) return x;
-  if (r == 2) return x * x;
-  return x > 0.f ? powf(x, rg) : 0.f;
-}
-
-// ---------------------------------------------------------------------------
-// 1a. Scores on the matrix cores (bfloat16 keys).
-//
-// v_mfma_f32_16x16x32_bf16 multiplies a 16x32 A by a 32x16 B.  B holds 16
-// tokens' keys for 32 coordinates: lane l supplies 8 consecutive
-// coordinates (one 16-byte load) of token l%16, block l/16.  A holds the
-// query: row 4*s + g is the s-th bfloat16 part of (alpha-1)*scale*q_g, where
-// q = part0 + part1 + part2 to float32 precision (each part is the bfloat16
-// rounding of what the previous parts left over); rows 12..15 are zero.
-// Products of bfloat16 values are exact and accumulate in float32, so
-// summing the three row results gives z to float32 accuracy.  Output lane l
-// holds rows 4*(l/16) + i of column l%16, i.e. part l/16 of head i.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int kb_of(int lane) { return lane >> 4; }
-
-__device__ __forceinline__ float bf16_part(float x, int part) {
-  const float p0 = static_cast<float>(static_cast<__bf16>(x));
-  const float r1 = x - p0;
-  const float p1 = static_cast<float>(static_cast<__bf16>(r1));
-  const float r2 = r1 - p1;
-  const float p2 = static_cast<float>(static_cast<__bf16>(r2));
-  return part == 0 ? p0 : part == 1 ? p1 : p2;
-}
-
-template <int D, int G>
-__device__ __forceinline__ void load_q_parts(bf16x8_t (&a)[(G + 3) / 4][D / 32],
-                                             const float *q, int b, int h,
-                                             int H, float zscale) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int n = lane & 15, kb = lane >> 4;
-  const int Hq = H * G;
-#pragma unroll
-  for (int ps = 0; ps < (G + 3) / 4; ++ps) {
-    const int part = n >> 2, g = (n & 3) + 4 * ps;
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = 0.f;
-        if (part < 3 && g < G)
-          x = bf16_part(q[(static_cast<size_t>(b) * Hq + h * G + g) * D +
-                          32 * s + 8 * kb + i] * zscale, part);
-        a[ps][s][i] = static_cast<__bf16>(x);
-      }
-  }
-}
-
-// Each wave takes a contiguous run of the flattened list of selected pages
-// (units in order, so a run seldom crosses into another unit) and walks it in
-// chunks of up to 64 pages.  A chunk's page references are loaded first, one
-// page per lane (selection entry, sequence length, then page-table entry),
-// and read back with readlane; its keys then stream in bodies of kKRing
-// 16-token groups (one page of 64 tokens, two of 32 or four of 16).  As soon
-// as a group has been used its registers are refilled with the same group of
-// the next body, so one body of keys is always in flight.  Every load in the
-// stream is unconditional (the refill after a chunk's last body repeats that
-// body and is never used), so the compiler's counts of loads in flight stay
-// exact and the wait for one group never waits for the groups behind it.
-constexpr int kKRing = 4;
-
-template <int D, int G, int P, bool SEL>
-__global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
-    const uint16_t *__restrict__ kpool, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, const float *__restrict__ q,
-    float zscale, int units, int H, int max_pages, int cap,
-    float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
-  constexpr int KS = D / 32;            // k-steps of 32 coordinates
-  constexpr int NPASS = (G + 3) / 4;    // groups of 4 query heads
-  constexpr int NT16 = P / 16;          // 16-token groups per page
-  constexpr int U = kKRing / NT16;      // pages per body
-  // the threshold step counts the heads it leaves to the apply step
-  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
-  static_assert(kKRing % NT16 == 0, "a body holds whole pages");
-  __shared__ int pref[kMaxUnits + 1];
-  __shared__ int tmp[kDecWaves];
-  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
-                                                   count, units, H, P, 1);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int n = lane & 15, kb = lane >> 4;
-  const int nwaves = gridDim.x * kDecWaves;
-  const int wg = blockIdx.x * kDecWaves + wave;
-  const int per = ((total + U - 1) / U + nwaves - 1) / nwaves;  // bodies
-  const int f0 = wg * per * U;
-  const int f1 = min(total, f0 + per * U);
-  if (f0 >= f1) return;  // whole waves; no block barrier follows
-
-  auto issue = [&](bf16x8_t (&bv)[KS], int slot, int h, int t) {
-    const uint16_t *row = kpool + pool_row(slot, h, 16 * t + n, H, P, D) + 8 * kb;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      bv[s] = *reinterpret_cast<const bf16x8_t *>(row + 32 * s);
-  };
-  auto lane_val = [](int x, int i) { return __builtin_amdgcn_readlane(x, i); };
-
-  bf16x8_t a[NPASS][KS];
-  bf16x8_t ring[kKRing][KS];
-  int cur_u = -1;
-  for (int c0 = f0; c0 < f1; c0 += kWave) {
-    const int nc = min(kWave, f1 - c0);        // pages in this chunk
-    const int nbc = (nc + U - 1) / U;          // bodies in this chunk
-    // page references, one page per lane (lanes past the chunk repeat its last)
-    const int f = c0 + min(lane, nc - 1);
-    const int ru = find_unit(pref, units, f);
-    const int rj = f - pref[ru];
-    const int rb = ru / H;
-    int rlp;
-    if constexpr (SEL) rlp = sel[static_cast<size_t>(ru) * max_pages + rj];
-    else rlp = rj;
-    const int rnt = page_tokens(rlp, seq_lens[rb], P);
-    const int rslot = page_table[static_cast<size_t>(rb) * max_pages + rlp];
-    auto body_page = [&](int k, int t) { return min(k * U + t, nc - 1); };
-#pragma unroll
-    for (int s = 0; s < kKRing; ++s) {
-      const int i = body_page(0, s / NT16);
-      issue(ring[s], lane_val(rslot, i), lane_val(ru, i) % H, s % NT16);
-    }
-    for (int k = 0; k < nbc; ++k) {
-      float pm[NPASS][4];
-#pragma unroll
-      for (int s = 0; s < kKRing; ++s) {
-        const int t = s / NT16, tt = s % NT16;
-        const int i = k * U + t;               // page of the chunk
-        const bool live = i < nc;
-        const int ic = min(i, nc - 1);
-        const int u = lane_val(ru, ic);
-        const int j = lane_val(rj, ic);
-        const int h = u % H;
-        if (tt == 0) {
-          if (u != cur_u) {  // rare: the run enters another unit
-            cur_u = u;
-            load_q_parts<D, G>(a, q, u / H, h, H, zscale);
-          }
-#pragma unroll
-          for (int ps = 0; ps < NPASS; ++ps)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pm[ps][e] = -FLT_MAX;
-        }
-        const bool valid = 16 * tt + n < lane_val(rnt, ic);
-        const __amdgpu_buffer_rsrc_t zr = store_rsrc(
-            zbuf + static_cast<size_t>(u) * G * cap,
-            static_cast<size_t>(G) * cap * sizeof(float));
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-          f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s2 = 0; s2 < KS; ++s2)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s2], ring[s][s2], c,
-                                                        0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p1 = __shfl_down(c[e], 16, kWave);
-            const float p2 = __shfl_down(c[e], 32, kWave);
-            const float z = c[e] + (p1 + p2);
-            const int g = 4 * ps + e;
-            if (g < G)
-              store_if(zr, 4 * (g * cap + j * P + 16 * tt + n), lane < 16 && live,
-                       valid ? z : -INFINITY);
-            if (valid) pm[ps][e] = fmaxf(pm[ps][e], z);
-          }
-        }
-        if (tt == NT16 - 1) {
-          // the page's maxima, lane g holding head g's
-          float mine = 0.f;
-#pragma unroll
-          for (int ps = 0; ps < NPASS; ++ps)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int g = 4 * ps + e;
-              if (g < G) {
-                const float m = group_max<16>(pm[ps][e]);
-                const float m0 = __shfl(m, 0, kWave);
-                mine = lane == g ? m0 : mine;
-              }
-            }
-          const int ps_ = pm_stride(max_pages);
-          const __amdgpu_buffer_rsrc_t pr = store_rsrc(
-              pmax + static_cast<size_t>(u) * G * ps_,
-              static_cast<size_t>(G) * ps_ * sizeof(float));
-          store_if(pr, 4 * (lane * ps_ + j), lane < G && live, mine);
-          const __amdgpu_buffer_rsrc_t sr = store_rsrc(
-              slots + static_cast<size_t>(u) * max_pages,
-              static_cast<size_t>(max_pages) * sizeof(int32_t));
-          store_if(sr, 4 * j, lane == 0 && live, lane_val(rslot, ic));
-        }
-        // refill: the same group of the next body
-        const int inx = body_page(k + 1, t);
-        issue(ring[s], lane_val(rslot, inx), lane_val(ru, inx) % H, tt);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 1b. Scores on the vector units (float32 keys).  One wave per page; D/8
-// lanes per token, 8 coordinates per lane.
-// ---------------------------------------------------------------------------
-template <class E, int D, int G>
-__global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
-    const typename E::T *__restrict__ kpool,
-    const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, const float *__restrict__ q,
-    float zscale, int units, int H, int P, int max_pages, int cap,
-    float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
-  constexpr int LPT = D / 8;
-  constexpr int TPW = kWave / LPT;
-  __shared__ int pref[kMaxUnits + 1];
-  __shared__ int tmp[kDecWaves];
-  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
-                                                   count, units, H, P, 1);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
-  const int Hq = H * G;
-  const int nwaves = gridDim.x * kDecWaves;
-  for (int f = blockIdx.x * kDecWaves + wave; f < total; f += nwaves) {
-    const PageRef r = page_ref(pref, units, f, page_table, seq_lens, sel, H, P,
-                               max_pages);
-    const int u = r.u, h = u % H, b = u / H;
-    float qs[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        qs[g][j] = q[(static_cast<size_t>(b) * Hq + h * G + g) * D + d0 + j] * zscale;
-    float mx[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) mx[g] = -FLT_MAX;
-    float *zu = zbuf + static_cast<size_t>(u) * G * cap +
-                static_cast<size_t>(r.j) * P;
-    for (int t0 = 0; t0 < P; t0 += TPW) {
-      const int t = t0 + sub;
-      float x[8];
-      load8(kpool + pool_row(r.slot, h, t, H, P, D) + d0, x);
-      const bool valid = t < r.nt;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[j], a);
-        a = group_sum<LPT>(a);
-        if (li == g) zu[static_cast<size_t>(g) * cap + t] = valid ? a : -INFINITY;
-        if (valid) mx[g] = fmaxf(mx[g], a);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m = group_max<kWave>(mx[g]);
-      if (lane == 0) pmax[(static_cast<size_t>(u) * G + g) * pm_stride(max_pages) + r.j] = m;
-    }
-    if (lane == 0) slots[static_cast<size_t>(u) * max_pages + r.j] = r.slot;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -866,10 +519,13 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     } else if (listed) {
       // Meanwhile the other waves bring the value rows of every candidate
       // (a superset of the support) into the L2, so that the gather after
-      // the solve does not wait on memory.  The loaded values are not used:
-      // the empty asm only keeps the loads.
-      constexpr int LPT = D / 8, TPW = kWave / LPT, KP = 16;
-      const int sub = lane / LPT, li = lane % LPT;
+      // the solve does not wait on memory: one 4-byte load per 128-byte line
+      // of a row.  The loaded values are not used: the empty asm only keeps
+      // the loads.
+      constexpr int ROWB = D * static_cast<int>(sizeof(typename E::T));
+      constexpr int LNR = ROWB >= 128 ? ROWB / 128 : 1;  // lines of a row
+      constexpr int TPW = kWave / LNR, KP = 4;             // rows per load
+      const int sub = lane / LNR, li = lane % LNR;
       int segs[NW + 1];
       segs[0] = 0;
 #pragma unroll
@@ -878,11 +534,11 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       const int n_all = segs[NW];
       const int h = u % H;
       for (int e0 = (wave - 1) * TPW + sub; e0 < n_all; e0 += (NW - 1) * TPW * KP) {
-        uint4 x[KP];
+        unsigned x[KP];
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
           const int e = e0 + k * (NW - 1) * TPW;
-          x[k] = make_uint4(0u, 0u, 0u, 0u);
+          x[k] = 0u;
           if (e < n_all) {
             int w = 0, base = 0;
 #pragma unroll
@@ -892,11 +548,11 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
             const int slot = dslot[pos >> lgP];
             const char *row = reinterpret_cast<const char *>(
                 vpool + pool_row(slot, h, pos & (P - 1), H, P, D));
-            x[k] = *reinterpret_cast<const uint4 *>(row + 16 * li);
+            x[k] = *reinterpret_cast<const unsigned *>(row + 128 * li);
           }
         }
 #pragma unroll
-        for (int k = 0; k < KP; ++k) asm volatile("" ::"v"(x[k].x));
+        for (int k = 0; k < KP; ++k) asm volatile("" ::"v"(x[k]));
       }
     }
     lds_barrier();
@@ -1054,7 +710,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     return;
   }
   constexpr int LPT = D / 8, TPW = kWave / LPT, RU = 8;
-  const int h = u % H, b = u / H;
+  const int h = u % H;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
   int nk = 0;
   {
@@ -1902,81 +1558,6 @@ static inline int exponent_code(float alpha, float &rg) {
   return 0;
 }
 
-// Persistent grid: enough blocks to fill the device, never more than items.
-static int persistent_blocks(size_t max_items, int per_cu) {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount,
-                            dev) != hipSuccess || n_cu <= 0)
-    n_cu = 256;
-  const size_t cap = static_cast<size_t>(n_cu) * per_cu;
-  if (max_items == 0) return 1;
-  return static_cast<int>(max_items < cap ? max_items : cap);
-}
-
-// Blocks of `kern` the device holds at once, at most `max_items`.
-template <class K>
-static int resident_blocks(K kern, int threads, size_t max_items) {
-  int dev = 0, n_cu = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount,
-                            dev) != hipSuccess || n_cu <= 0)
-    n_cu = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void *>(kern), threads, 0) !=
-          hipSuccess || per_cu <= 0)
-    per_cu = 1;
-  const size_t cap = static_cast<size_t>(n_cu) * per_cu;
-  if (max_items == 0) return 1;
-  return static_cast<int>(max_items < cap ? max_items : cap);
-}
-
-template <class E, int D, int G>
-hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
-                                float scale, float alpha, const int32_t *sel,
-                                const int32_t *count, void *ws,
-                                hipStream_t stream) {
-  const DecodeWs L = decode_ws_layout(kv);
-  char *w = static_cast<char *>(ws);
-  const int units = kv.batch * kv.num_kv_heads;
-  const size_t pages = static_cast<size_t>(units) * kv.max_pages;
-  const int blocks = persistent_blocks((pages + kDecWaves - 1) / kDecWaves, 4);
-  const int cap = kv.max_pages * kv.page_size;
-  float *z = reinterpret_cast<float *>(w + L.z);
-  float *pm = reinterpret_cast<float *>(w + L.cmax);
-  int32_t *sl = reinterpret_cast<int32_t *>(w + L.slot);
-  int32_t *und = reinterpret_cast<int32_t *>(w + L.ctr) + units;
-  const float zs = (alpha - 1.0f) * scale;
-  if constexpr (sizeof(typename E::T) == 2) {
-    const uint16_t *k = static_cast<const uint16_t *>(kv.k);
-    // resident waves walk contiguous runs of pages
-    auto go = [&](auto kern) {
-      const int nb = resident_blocks(kern, kDecThreads,
-                                     (pages + kDecWaves - 1) / kDecWaves);
-      hipLaunchKernelGGL(kern, dim3(nb), dim3(kDecThreads), 0, stream, k,
-                         kv.page_table, kv.seq_lens, sel, count, q, zs, units,
-                         kv.num_kv_heads, kv.max_pages, cap, z, pm, sl, und);
-    };
-    auto by_page = [&](auto has_sel) {
-      constexpr bool S = decltype(has_sel)::value;
-      switch (kv.page_size) {
-        case 16: go(k_entmax_scores_mfma<D, G, 16, S>); break;
-        case 32: go(k_entmax_scores_mfma<D, G, 32, S>); break;
-        default: go(k_entmax_scores_mfma<D, G, 64, S>); break;
-      }
-    };
-    if (sel) by_page(std::true_type());
-    else by_page(std::false_type());
-  } else {
-    hipLaunchKernelGGL((k_entmax_scores_valu<E, D, G>), dim3(blocks),
-                       dim3(kDecThreads), 0, stream,
-                       static_cast<const typename E::T *>(kv.k), kv.page_table,
-                       kv.seq_lens, sel, count, q, zs, units, kv.num_kv_heads,
-                       kv.page_size, kv.max_pages, cap, z, pm, sl, und);
-  }
-  return hipGetLastError();
-}
-
 template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,
@@ -2080,9 +1661,6 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
 }
 
 #define EKV_INST_DEC(E, D, G)                                                \
-  template hipError_t launch_entmax_scores<E, D, G>(                         \
-      const ekv_paged_kv &, const float *, float, float, const int32_t *,    \
-      const int32_t *, void *, hipStream_t);                                 \
   template hipError_t launch_entmax_threshold<E, D, G>(                      \
       const ekv_paged_kv &, float, const int32_t *, const int32_t *, float *, \
       float *, void *, hipStream_t);                                         \
