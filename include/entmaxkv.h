@@ -157,6 +157,25 @@ ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
                            float *ub, float *gstat, void *stream);
 
 /*
+ * ekv_refresh_score_pages - the metadata refresh and the scoring of one
+ * decode step in one call (Technical Summary, §2.A: metadata kept up to date
+ * as tokens arrive, then query-aware scoring).  For every sequence b with
+ * seq_lens[b] > 0, the metadata of its last logical page (the page the
+ * newest token went to) is rebuilt for every KV head, bit-identical to
+ * ekv_build_meta; then the pages are scored exactly as by ekv_score_pages.
+ * It replaces ekv_build_meta(first_page[b] = (seq_lens[b]-1)/P, span 1)
+ * followed by ekv_score_pages, for steps that append at most one page's
+ * worth of tokens per sequence, all of them to its last page.  Both parts
+ * of *meta that are non-NULL are refreshed; k must be non-NULL and 16-byte
+ * aligned.  Arguments as for ekv_score_pages.  Usually one kernel on the
+ * stream (each sequence's last tile is scored by the wave that rebuilt it);
+ * two when batch * num_kv_heads exceeds the waves the device holds.
+ */
+ekv_status ekv_refresh_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
+                                   const float *q, float scale, int32_t mode,
+                                   float *ub, float *gstat, void *stream);
+
+/*
  * ekv_select_topk - fixed-budget selection (Technical Summary, §2.B.1).
  * For each unit, ranks pages by the largest bound over its G query heads
  * and keeps the min(k, n_pages) highest; equal bounds favour the lower page

@@ -60,6 +60,9 @@ _SIGNATURES = {
     "ekv_score_pages": (_c_i32, [ctypes.POINTER(ekv_paged_kv),
                                  ctypes.POINTER(ekv_meta), _c_p, _c_f32, _c_i32,
                                  _c_p, _c_p, _c_p]),
+    "ekv_refresh_score_pages": (_c_i32, [ctypes.POINTER(ekv_paged_kv),
+                                 ctypes.POINTER(ekv_meta), _c_p, _c_f32, _c_i32,
+                                 _c_p, _c_p, _c_p]),
     "ekv_select_topk": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_i32,
                                  _c_p, _c_p, _c_p, _c_size, _c_p]),
     "ekv_select_gauss": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
@@ -211,6 +214,16 @@ def ekv_score_pages(kv: PagedKV, bbox, gauss, q, scale: float, mode: int,
     _check(load_library().ekv_score_pages(
         ctypes.byref(s), ctypes.byref(m), _ptr(q), float(scale), int(mode),
         _ptr(ub), _ptr(gstat), _stream(stream)), "ekv_score_pages")
+
+
+def ekv_refresh_score_pages(kv: PagedKV, bbox, gauss, q, scale: float,
+                            mode: int, ub=None, gstat=None,
+                            stream=None) -> None:
+    """Rebuild every sequence's last-page metadata, then score the pages."""
+    s, m = kv.struct(), _meta(bbox, gauss)
+    _check(load_library().ekv_refresh_score_pages(
+        ctypes.byref(s), ctypes.byref(m), _ptr(q), float(scale), int(mode),
+        _ptr(ub), _ptr(gstat), _stream(stream)), "ekv_refresh_score_pages")
 
 
 def ekv_select_topk(kv: PagedKV, ub, k: int, sel, count, ws,

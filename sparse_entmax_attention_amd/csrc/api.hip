@@ -198,10 +198,12 @@ ekv_status ekv_build_meta(const ekv_paged_kv *kv, const int32_t *first_page,
   return hip_status(e, "ekv_build_meta launch");
 }
 
-ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
-                           const float *q, float scale, int32_t mode,
-                           float *ub, float *gstat, void *stream) {
-  EKV_TRY(check_kv(kv, false, false));
+namespace {
+ekv_status score_pages(const char *who, const ekv_paged_kv *kv,
+                       const ekv_meta *meta, const float *q, float scale,
+                       int32_t mode, float *ub, float *gstat, bool refresh,
+                       void *stream) {
+  EKV_TRY(check_kv(kv, refresh, false));
   EKV_TRY(check_scale(scale));
   if (!meta || !q) return fail(EKV_ERR_INVALID_ARG, "meta and q are required");
   if (mode <= 0 || (mode & ~(EKV_SCORE_BBOX | EKV_SCORE_GAUSS)))
@@ -217,9 +219,25 @@ ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
   const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
     return ekv::launch_score<decltype(E), decltype(D)::value,
                              decltype(G)::value>(*kv, *meta, q, scale, mode,
-                                                 ub, gstat, as_stream(stream));
+                                                 ub, gstat, refresh,
+                                                 as_stream(stream));
   });
-  return hip_status(e, "ekv_score_pages launch");
+  return hip_status(e, who);
+}
+}  // namespace
+
+ekv_status ekv_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
+                           const float *q, float scale, int32_t mode,
+                           float *ub, float *gstat, void *stream) {
+  return score_pages("ekv_score_pages launch", kv, meta, q, scale, mode, ub,
+                     gstat, false, stream);
+}
+
+ekv_status ekv_refresh_score_pages(const ekv_paged_kv *kv, const ekv_meta *meta,
+                                   const float *q, float scale, int32_t mode,
+                                   float *ub, float *gstat, void *stream) {
+  return score_pages("ekv_refresh_score_pages launch", kv, meta, q, scale,
+                     mode, ub, gstat, true, stream);
 }
 
 ekv_status ekv_select_topk(const ekv_paged_kv *kv, const float *ub, int32_t k,

@@ -58,7 +58,7 @@ hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
 template <class E, int D, int G>
 hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
                         const float *q, float scale, int mode, float *ub,
-                        float *gstat, hipStream_t stream);
+                        float *gstat, bool refresh, hipStream_t stream);
 template <int G>
 hipError_t launch_select_topk(const ekv_paged_kv &kv, const float *ub, int k,
                               int32_t *sel, int32_t *count, void *ws,

@@ -31,8 +31,9 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
     const typename E::T *__restrict__ kpool,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ first_page, int H, int P, int max_pages,
-    typename E::T *__restrict__ bbox, float *__restrict__ gauss) {
+    const int32_t *__restrict__ first_page, int last_only, int H, int P,
+    int max_pages, typename E::T *__restrict__ bbox,
+    float *__restrict__ gauss) {
   constexpr int CG = D / 8;                 // coordinate groups
   constexpr int TG = kMetaThreads / CG;     // token groups
   constexpr int MAXT = (64 + TG - 1) / TG;  // tokens per thread (P <= 64)
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
   const int cg = threadIdx.x % CG, tg = threadIdx.x / CG, d0 = cg * 8;
   const int len = seq_lens[b];
   const int np = n_pages_of(len, P);
-  int p0 = first_page ? first_page[b] : 0;
+  int p0 = last_only ? np - 1 : first_page ? first_page[b] : 0;
   if (p0 < 0) p0 = 0;
   for (int lp = p0 + blockIdx.x; lp < np; lp += gridDim.x) {
     const int slot = page_table[static_cast<size_t>(b) * max_pages + lp];
@@ -217,13 +218,96 @@ struct ScoreItem {
   int b, h, tile, np;
 };
 
-template <class E, int D, int G, int MODE>
+// Rebuild of one page's metadata for one KV head by a single wave, equal bit
+// for bit to what k_build_meta computes: per coordinate, partial sums over
+// the token groups tg, tg + TG, ... of a k_build_meta block, each taken in
+// token order from zero, then added in group order; the variance the same
+// way about the mean; minima and maxima do not depend on order.  Lane l
+// owns coordinates l*CPL .. l*CPL + CPL - 1 and holds all n <= 64 tokens of
+// them.  Null bbox or gauss skips that part.
+template <class E, int D>
+__device__ __forceinline__ void rebuild_page_meta(const typename E::T *kpool, int slot, int h,
+                                  int H, int P, int n, typename E::T *bbox,
+                                  float *gauss) {
+  using T = typename E::T;
+  constexpr int CPL = D / kWave;            // coordinates per lane
+  constexpr int CG = D / 8;                 // coordinate groups of a block
+  constexpr int TG = kMetaThreads / CG;     // token groups of a block
+  constexpr int MAXT = (64 + TG - 1) / TG;  // tokens per group (P <= 64)
+  const int lane = threadIdx.x & (kWave - 1);
+  // The page's n valid rows as a range-checked buffer: rows past n read as
+  // zero (and are masked below), so all 64 loads are unconditional and in
+  // flight at once, each with the lane's offset and a constant row offset.
+  const __amdgpu_buffer_rsrc_t rows = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(kpool + pool_row(slot, h, 0, H, P, D)),
+      static_cast<short>(0), n * D * static_cast<int>(sizeof(T)), 0x00020000);
+  // One coordinate at a time, its n tokens in registers (the second read of
+  // the rows comes from the cache).
+#pragma unroll 1
+  for (int c = 0; c < CPL; ++c) {
+    const int voff = (lane * CPL + c) * static_cast<int>(sizeof(T));
+    float x[64];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+      const int soff = t * D * static_cast<int>(sizeof(T));
+      if constexpr (sizeof(T) == 2)
+        x[t] = __uint_as_float(static_cast<uint32_t>(
+                                   __builtin_amdgcn_raw_buffer_load_b16(rows, voff, soff, 0))
+                               << 16);
+      else
+        x[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows, voff, soff, 0));
+    }
+    float mn = INFINITY, mx = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXT; ++i) {
+        const int t = tg + i * TG;
+        if (t < 64 && t < n) {
+          mn = fminf(mn, x[t]);
+          mx = fmaxf(mx, x[t]);
+          part += x[t];
+        }
+      }
+      s = tg == 0 ? part : s + part;
+    }
+    const float mean = s / static_cast<float>(n);
+    float v = 0.f;
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXT; ++i) {
+        const int t = tg + i * TG;
+        if (t < 64 && t < n) {
+          const float dv = x[t] - mean;
+          part = fmaf(dv, dv, part);
+        }
+      }
+      v = tg == 0 ? part : v + part;
+    }
+    const int d = lane * CPL + c;
+    if (bbox) {
+      store1(bbox + meta_row(slot, h, 0, H, D) + d, mn);
+      store1(bbox + meta_row(slot, h, 1, H, D) + d, mx);
+    }
+    if (gauss) {
+      gauss[meta_row(slot, h, 0, H, D) + d] = mean;
+      gauss[meta_row(slot, h, 1, H, D) + d] = v / static_cast<float>(n);
+    }
+  }
+}
+
+template <class E, int D, int G, int MODE, bool REFRESH>
 __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, MODE>())) void k_score(
-    const typename E::T *__restrict__ bbox, const float *__restrict__ gauss,
+    const typename E::T *bbox, const float *gauss,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const float *__restrict__ q,
     float scale, int H, int P, int max_pages, int batch,
-    float *__restrict__ ub, float *__restrict__ gstat) {
+    float *__restrict__ ub, float *__restrict__ gstat,
+    const typename E::T *__restrict__ kpool, typename E::T *bbox_w,
+    float *gauss_w) {
   using T = typename E::T;
   constexpr bool kBox = (MODE & EKV_SCORE_BBOX) != 0;
   constexpr bool kGauss = (MODE & EKV_SCORE_GAUSS) != 0;
@@ -235,51 +319,81 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   static_assert(kScoreTile == kWave, "one page-table entry per lane");
   static_assert(NSTEP >= R, "the ring must fit in a tile");
   static_assert(QF == 1 || QF == 2 || QF % 4 == 0, "query staging width");
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  // the wave index (and everything derived from it) is wave-uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int sub = lane / LPP, li = lane % LPP;
   const int Hq = H * G;
   const int n_tiles = (max_pages + kScoreTile - 1) / kScoreTile;
 
-  // LDS: per wave G*D staged query floats, then the per-sequence tile prefix
-  // (batch + 1 entries) and page counts (batch entries).
+  constexpr bool refresh = REFRESH;
+  // LDS: per wave G*D staged query floats, then per sequence the prefix of
+  // its tiles (batch + 1 entries), its page count (batch entries) and, when
+  // refreshing, the prefix of non-empty sequences (batch + 1 entries).  When
+  // refreshing, the last tile of every non-empty sequence comes first in the
+  // numbering (and the main prefix counts the other tiles), so that each is
+  // the first item of some wave (the host checks there are enough waves).
   extern __shared__ float4 s_dyn4[];
   float *s_q = reinterpret_cast<float *>(s_dyn4) + wave * G * D;
   int *s_pref = reinterpret_cast<int *>(s_dyn4) + kScoreWaves * G * D;
   int *s_np = s_pref + batch + 1;
+  int *s_plast = s_np + batch;
   __shared__ int s_tmp[kScoreWaves];
   {
     const int per = (batch + kScoreThreads - 1) / kScoreThreads;
     const int b0 = min(batch, threadIdx.x * per), b1 = min(batch, b0 + per);
-    int local = 0;
+    auto tiles_main = [&](int np) {
+      const int nt = (np + kScoreTile - 1) / kScoreTile;
+      return refresh ? max(nt - 1, 0) : nt;
+    };
+    int local = 0, local_last = 0;
     for (int b = b0; b < b1; ++b) {
       // pages of sequence b, clamped to its page-table row
       const int np = max(0, min(n_pages_of(seq_lens[b], P), max_pages));
       s_np[b] = np;
-      local += (np + kScoreTile - 1) / kScoreTile;
+      local += tiles_main(np);
+      local_last += refresh && np > 0;
     }
-    int total;
+    int total, total_last = 0, base_last = 0;
     int base = block_excl_scan<kScoreThreads>(local, s_tmp, total);
+    if constexpr (REFRESH)
+      base_last = block_excl_scan<kScoreThreads>(local_last, s_tmp, total_last);
     for (int b = b0; b < b1; ++b) {
       s_pref[b] = base;
-      base += (s_np[b] + kScoreTile - 1) / kScoreTile;
+      base += tiles_main(s_np[b]);
+      s_plast[b] = base_last;
+      base_last += refresh && s_np[b] > 0;
     }
-    if (threadIdx.x == 0) s_pref[batch] = total;
+    if (threadIdx.x == 0) {
+      s_pref[batch] = total;
+      s_plast[batch] = total_last;
+    }
     lds_barrier();
   }
-  const int n_items = s_pref[batch] * H;
+  const int n_last = REFRESH ? s_plast[batch] : 0;
+  const int n_items = (s_pref[batch] + n_last) * H;
   const int n_waves = gridDim.x * kScoreWaves;
   int it = blockIdx.x * kScoreWaves + wave;
   if (it >= n_items) return;  // whole waves; no block barrier follows
 
-  int bscan = 0;  // items only move forward, and so does their sequence
+  // items only move forward, and so do their sequences in each part
+  int blast = 0, bscan = 0;
   auto describe = [&](int i) {
     const int ts = i / H;
-    while (s_pref[bscan + 1] <= ts) ++bscan;
     ScoreItem d;
-    d.b = __builtin_amdgcn_readfirstlane(bscan);
     d.h = i - ts * H;
-    d.tile = __builtin_amdgcn_readfirstlane(ts - s_pref[bscan]);
-    d.np = __builtin_amdgcn_readfirstlane(s_np[bscan]);
+    if (REFRESH && ts < n_last) {  // a sequence's last tile (refreshing only)
+      while (s_plast[blast + 1] <= ts) ++blast;
+      d.b = __builtin_amdgcn_readfirstlane(blast);
+      d.np = __builtin_amdgcn_readfirstlane(s_np[blast]);
+      d.tile = (d.np - 1) / kScoreTile;
+    } else {
+      const int tm = ts - n_last;
+      while (s_pref[bscan + 1] <= tm) ++bscan;
+      d.b = __builtin_amdgcn_readfirstlane(bscan);
+      d.np = __builtin_amdgcn_readfirstlane(s_np[bscan]);
+      d.tile = __builtin_amdgcn_readfirstlane(tm - s_pref[bscan]);
+    }
     return d;
   };
   // Slot of page (tile * 64 + lane), clamped to the sequence's last page.
@@ -322,6 +436,20 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
 
   float qv[QF];
   ScoreItem cur = describe(it);
+  if (REFRESH && it < n_last * H) {
+    // This wave's first tile is the last tile of its sequence: rebuild the
+    // metadata of the sequence's last page for this KV head before any of
+    // the tile's records is read.  The fence makes the wave's stores visible
+    // to its own later loads.
+    // (read by every lane from one address: uniform, kept in scalars)
+    const int lp = cur.np - 1;
+    const int slot = __builtin_amdgcn_readfirstlane(
+        page_table[static_cast<size_t>(cur.b) * max_pages + lp]);
+    const int n = __builtin_amdgcn_readfirstlane(page_tokens(lp, seq_lens[cur.b], P));
+    rebuild_page_meta<E, D>(kpool, slot, cur.h, H, P, n, bbox_w, gauss_w);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
   int slots_cur = load_slots(cur);
   load_q(cur, qv);
   stage_q(qv);
@@ -463,7 +591,7 @@ hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
   dim3 grid(pages, kv.num_kv_heads, kv.batch);
   hipLaunchKernelGGL((k_build_meta<E, D>), grid, dim3(kMetaThreads), 0, stream,
                      static_cast<const typename E::T *>(kv.k), kv.page_table,
-                     kv.seq_lens, first_page, kv.num_kv_heads, kv.page_size,
+                     kv.seq_lens, first_page, 0, kv.num_kv_heads, kv.page_size,
                      kv.max_pages, static_cast<typename E::T *>(meta.bbox),
                      meta.gauss);
   return hipGetLastError();
@@ -471,38 +599,69 @@ hipError_t launch_build_meta(const ekv_paged_kv &kv, const int32_t *first_page,
 
 // Waves stay resident and walk their tiles; the grid is as many blocks as fit
 // on the device at once (fewer if there are fewer tiles than waves).
+// With `refresh`, the metadata of every sequence's last page is rebuilt
+// first: inside the scoring launch when every (sequence, KV head) gets a
+// wave of its own, else by a one-page metadata launch before it.
 template <class E, int D, int G>
 hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
                         const float *q, float scale, int mode, float *ub,
-                        float *gstat, hipStream_t stream) {
+                        float *gstat, bool refresh, hipStream_t stream) {
+  using T = typename E::T;
   const long long items = static_cast<long long>(page_tiles(kv)) *
                           kv.num_kv_heads * kv.batch;
   const size_t lds = static_cast<size_t>(kScoreWaves) * G * D * sizeof(float) +
-                     (2 * static_cast<size_t>(kv.batch) + 1) * sizeof(int);
-  auto launch = [&](auto kern) {
-    int dev = 0, n_cu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
-            hipSuccess || n_cu <= 0)
-      n_cu = 256;
+                     (3 * static_cast<size_t>(kv.batch) + 2) * sizeof(int);
+  hipError_t err = hipSuccess;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  auto grid_of = [&](auto kern) {
+    int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void *>(kern), kScoreThreads, lds) !=
             hipSuccess || per_cu <= 0)
       per_cu = 1;
     const long long want = (items + kScoreWaves - 1) / kScoreWaves;
-    const int blocks = static_cast<int>(
+    return static_cast<int>(
         std::min<long long>(want, static_cast<long long>(n_cu) * per_cu));
+  };
+  auto launch = [&](auto kern, int blocks) {
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(kScoreThreads), lds, stream,
-                       static_cast<const typename E::T *>(meta.bbox),
-                       meta.gauss, kv.page_table, kv.seq_lens, q, scale,
-                       kv.num_kv_heads, kv.page_size, kv.max_pages, kv.batch,
-                       ub, gstat);
+                       static_cast<const T *>(meta.bbox), meta.gauss,
+                       kv.page_table, kv.seq_lens, q, scale, kv.num_kv_heads,
+                       kv.page_size, kv.max_pages, kv.batch, ub, gstat,
+                       static_cast<const T *>(kv.k), static_cast<T *>(meta.bbox),
+                       meta.gauss);
+    err = hipGetLastError();
+  };
+  // the fused form needs a wave for every (sequence, KV head)
+  auto run = [&](auto plain, auto fused) {
+    if (refresh) {
+      const int nb = grid_of(fused);
+      if (static_cast<long long>(kv.batch) * kv.num_kv_heads <=
+          static_cast<long long>(nb) * kScoreWaves) {
+        launch(fused, nb);
+        return;
+      }
+      hipLaunchKernelGGL((k_build_meta<E, D>), dim3(1, kv.num_kv_heads, kv.batch),
+                         dim3(kMetaThreads), 0, stream,
+                         static_cast<const T *>(kv.k), kv.page_table,
+                         kv.seq_lens, nullptr, 1, kv.num_kv_heads, kv.page_size,
+                         kv.max_pages, static_cast<T *>(meta.bbox), meta.gauss);
+      if ((err = hipGetLastError()) != hipSuccess) return;
+    }
+    launch(plain, grid_of(plain));
   };
   constexpr int kBoth = EKV_SCORE_BBOX | EKV_SCORE_GAUSS;
-  if (mode == EKV_SCORE_BBOX) launch(k_score<E, D, G, EKV_SCORE_BBOX>);
-  else if (mode == EKV_SCORE_GAUSS) launch(k_score<E, D, G, EKV_SCORE_GAUSS>);
-  else launch(k_score<E, D, G, kBoth>);
-  return hipGetLastError();
+  if (mode == EKV_SCORE_BBOX)
+    run(k_score<E, D, G, EKV_SCORE_BBOX, false>, k_score<E, D, G, EKV_SCORE_BBOX, true>);
+  else if (mode == EKV_SCORE_GAUSS)
+    run(k_score<E, D, G, EKV_SCORE_GAUSS, false>, k_score<E, D, G, EKV_SCORE_GAUSS, true>);
+  else
+    run(k_score<E, D, G, kBoth, false>, k_score<E, D, G, kBoth, true>);
+  return err;
 }
 
 #define EKV_INST_META(E, D)                                                 \
@@ -512,7 +671,7 @@ hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
 #define EKV_INST_SCORE(E, D, G)                                             \
   template hipError_t launch_score<E, D, G>(                                \
       const ekv_paged_kv &, const ekv_meta &, const float *, float, int,    \
-      float *, float *, hipStream_t);
+      float *, float *, bool, hipStream_t);
 
 EKV_FOR_EACH_ED(EKV_INST_META)
 EKV_FOR_EACH_EDG(EKV_INST_SCORE)

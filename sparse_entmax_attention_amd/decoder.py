@@ -68,6 +68,16 @@ class DecodeBuffers:
                           self.gstat_buf if mode & B.EKV_SCORE_GAUSS else None,
                           stream)
 
+    def refresh_score(self, q, mode: int, stream=None):
+        """The last page of every sequence gets fresh metadata, then every
+        page is scored (one token appended per sequence since the last
+        step)."""
+        B.ekv_refresh_score_pages(self.kv, self.bbox, self.gauss, q, self.scale,
+                                  mode,
+                                  self.ub_buf if mode & B.EKV_SCORE_BBOX else None,
+                                  self.gstat_buf if mode & B.EKV_SCORE_GAUSS else None,
+                                  stream)
+
     def select_topk(self, k: int, stream=None):
         B.ekv_select_topk(self.kv, self.ub_buf, k, self.sel, self.count,
                           self.ws_topk, stream)
