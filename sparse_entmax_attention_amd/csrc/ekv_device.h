@@ -193,6 +193,12 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   x += dpp_rows_d<kDppRowBcast31, 0xC>(x);
   return readlane_d(x, kWave - 1);
 }
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x = group_sum<16>(x);
+  x += __int_as_float(dpp_rows<kDppRowBcast15, 0xA>(__float_as_int(x), 0));
+  x += __int_as_float(dpp_rows<kDppRowBcast31, 0xC>(__float_as_int(x), 0));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
 __device__ __forceinline__ int wave_sum_i(int x) {
   x = group_sum_i<16>(x);
   x += dpp_rows<kDppRowBcast15, 0xA>(x, 0);

@@ -494,21 +494,37 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
   }
   lds_barrier();
 
-  // 4. Newton on F^(1/r) - 1 from tau_lo; one wave reduction and one
-  // barrier per iteration (s_fd is double-buffered).
+  // 4. Newton on F^(1/r) - 1 from tau_lo.  The step for r = 2,
+  // 2 (F - sqrt F) / (-F'), is taken as 2 sqrt(F) (F - 1) / ((sqrt F + 1)
+  // (-F')), which keeps its relative accuracy in float32 as F -> 1; every
+  // thread takes the same step from the same sums.  All waves share the
+  // pages, with one barrier per iteration (s_fd is double-buffered).
+  auto step_from = [&](float ff, float dd, float t, float &next) {
+    if (!(ff > 1.0f) || !(dd > 0.0f)) return false;
+    float step;
+    if (r == 2) {
+      const float sf = sqrtf(ff);
+      step = 2.0f * sf * (ff - 1.0f) / ((sf + 1.0f) * dd);
+    } else {
+      step = (ff - 1.0f) / dd;
+    }
+    next = t + step;
+    return next > t;
+  };
+  auto page_terms = [&](int i, float t, float &f, float &df) {
+    const float2 e = i < kGtSvItems ? s_sv[i * kPageTile + lane]
+                                    : surv_entry(surv_tile(i) * kPageTile + lane);
+    if (e.x == -INFINITY) return;
+    const bool last = e.y < 0.f;
+    gauss_term(e.x, last ? -1.0f - e.y : e.y,
+               last ? last_n : static_cast<float>(P), t, r, f, df);
+  };
   float tau = tau_lo;
   for (int it = 0; it < 64; ++it) {
     float f = 0.f, df = 0.f;
-    for (int i = wave; i < n_st; i += kGtWaves) {
-      const float2 e = i < kGtSvItems ? s_sv[i * kPageTile + lane]
-                                      : surv_entry(surv_tile(i) * kPageTile + lane);
-      if (e.x == -INFINITY) continue;
-      const bool last = e.y < 0.f;
-      gauss_term(e.x, last ? -1.0f - e.y : e.y,
-                 last ? last_n : static_cast<float>(P), tau, r, f, df);
-    }
-    f = group_sum<kWave>(f);
-    df = group_sum<kWave>(df);
+    for (int i = wave; i < n_st; i += kGtWaves) page_terms(i, tau, f, df);
+    f = wave_sum_f(f);
+    df = wave_sum_f(df);
     if (lane == 0) s_fd[it & 1][wave] = make_float2(f, df);
     lds_barrier();
     float ff = 0.f, dd = 0.f;
@@ -518,12 +534,8 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
       ff += v.x;
       dd += v.y;
     }
-    // Every thread takes the same step from the same sums.
-    if (!(ff > 1.0f) || !(dd > 0.0f)) break;
-    const double F = ff;
-    const double step = (r == 2) ? 2.0 * (F - sqrt(F)) / dd : (F - 1.0) / dd;
-    const float next = static_cast<float>(static_cast<double>(tau) + step);
-    if (!(next > tau)) break;
+    float next;
+    if (!step_from(ff, dd, tau, next)) break;
     tau = next;
   }
   if (tid == 0) tau_hat[row] = tau;
