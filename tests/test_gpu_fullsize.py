@@ -176,3 +176,43 @@ def test_ragged_pool_b16_appends_sampled(gpu):
     for b, h in [(0, 0), (7, 4), (15, 7)]:
         print("[unit] b=%d h=%d len=%d" % (b, h, inp.lens[b]), flush=True)
         check_gauss_unit(buf, inp, b, h, alpha, spec.delta)
+
+
+def test_cluster_1m_appended_fused_refresh_phases(gpu):
+    # The 1M-token cache with one token appended (it opens a new 64-token
+    # page), stepped the way the benchmark's Gaussian leg does it: the tail
+    # page's refresh inside the scoring launch, then the selector and the
+    # three decode phases as separate calls.
+    spec = workloads.workload("cluster_1m", spare_pages=1)
+    print("[case] cluster_1m + 1 token, seed 3001, fused refresh + phases",
+          flush=True)
+    inp = workloads.generate(spec, 3001, gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(3001)
+    workloads.append_token(inp, gen)
+    workloads.draw_fresh_queries(inp, gen)
+    alpha = spec.alphas[0]
+    buf.refresh_score(inp.q, ekv.EKV_SCORE_GAUSS)
+    buf.select_gauss(alpha, spec.delta)
+    ekv.ekv_entmax_scores(kv, inp.q, buf.scale, alpha, buf.sel, buf.count,
+                          buf.ws_decode)
+    ekv.ekv_entmax_threshold(kv, alpha, buf.sel, buf.count, buf.tau, buf.out,
+                             buf.ws_decode)
+    ekv.ekv_entmax_apply(kv, alpha, buf.sel, buf.count, buf.out, None,
+                         buf.ws_decode)
+    torch.cuda.synchronize()
+    assert inp.lens[0] == spec.seq_len + 1
+    # the new page (one token) equals a full rebuild of it
+    full = ekv.DecodeBuffers(paged_kv(inp))
+    full.build_meta()
+    torch.cuda.synchronize()
+    tail = inp.page_table[0, spec.seq_len // spec.page_size].long()
+    assert torch.equal(buf.bbox[tail], full.bbox[tail])
+    assert torch.equal(buf.gauss[tail], full.gauss[tail])
+    del full
+    for b, h in [(0, 3), (0, 7)]:
+        print("[unit] b=%d h=%d" % (b, h), flush=True)
+        check_gauss_unit(buf, inp, b, h, alpha, spec.delta)
