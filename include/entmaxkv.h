@@ -242,13 +242,16 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
  *   ekv_entmax_scores     gathers the selected keys and writes z to the
  *                         workspace with per-chunk maxima.
  *   ekv_entmax_threshold  solves tau per query head (tau may be NULL: it is
- *                         then kept in the workspace only) and, for every
- *                         head whose candidate scores fit on chip (the usual
- *                         case), gathers the values of the support and
- *                         writes that head's row of out.
+ *                         then kept in the workspace only) and gathers the
+ *                         values of the support: with a selection (sel not
+ *                         NULL) it writes every row of out; over the full
+ *                         cache, the rows of the heads whose candidate
+ *                         scores fit on chip (the usual case).
  *   ekv_entmax_apply      writes the remaining rows of out (all rows, and
  *                         probs, when probs is not NULL), reading values
- *                         only for tokens with p_i > 0.
+ *                         only for tokens with p_i > 0.  With a selection
+ *                         and probs NULL nothing remains: it returns
+ *                         EKV_OK without launching any work.
  */
 ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,

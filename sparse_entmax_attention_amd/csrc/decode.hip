@@ -219,7 +219,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   __shared__ int s_npg[NW];
   __shared__ int dense[kTauPageCap];   // listed pages (selection index j)
   __shared__ int dslot[kTauPageCap];   // their pool slots
-  __shared__ float red_f[NW];
+  __shared__ float s_wmax[NW];
+  __shared__ int s_wscan[NW];
+  __shared__ double s_wL[NW];
   __shared__ int red_i[NW];
   __shared__ double red_d[NW];
   __shared__ long long red_ll[NW];
@@ -253,18 +255,30 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     pv[4 * k] = v.x; pv[4 * k + 1] = v.y; pv[4 * k + 2] = v.z; pv[4 * k + 3] = v.w;
   }
   const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+  // Slices k (4 kTauThreads pages each) that hold selected pages: the others
+  // are skipped (the test is uniform, and no load depends on it).
+  const int nsl = min(U4, (cnt + 4 * kTauThreads - 1) / (4 * kTauThreads));
 #pragma unroll
   for (int k = 0; k < U4; ++k)
+    if (k < nsl)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (page_k(k, e) >= cnt) pv[4 * k + e] = -FLT_MAX;
+      for (int e = 0; e < 4; ++e)
+        if (page_k(k, e) >= cnt) pv[4 * k + e] = -FLT_MAX;
   for (int i = tid; i < kTauMaxBins; i += kTauThreads) hist[i] = 0u;
-  // Largest score.
+  // Largest score (the barrier also orders the clearing of hist).
   float mloc = -FLT_MAX;
 #pragma unroll
-  for (int k = 0; k < U; ++k) mloc = fmaxf(mloc, pv[k]);
+  for (int k = 0; k < U4; ++k)
+    if (k < nsl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, pv[4 * k + e]);
   for (int j = CACHED + tid; j < cnt; j += kTauThreads) mloc = fmaxf(mloc, pm[j]);
-  const float M = block_max<kTauThreads>(mloc, red_f);  // also orders hist
+  mloc = wave_max_f(mloc);
+  if (lane == 0) s_wmax[wave] = mloc;
+  lds_barrier();
+  float M = s_wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_wmax[w]);
   const double Md = M;
 
   // Tighter lower bracket from the page maxima within 1 of M: with C_b the
@@ -278,16 +292,24 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     }
   };
 #pragma unroll
-  for (int k = 0; k < U; ++k) count_max(pv[k]);
+  for (int k = 0; k < U4; ++k)
+    if (k < nsl)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) count_max(pv[4 * k + e]);
   for (int j = CACHED + tid; j < cnt; j += kTauThreads) count_max(pm[j]);
   lds_barrier();
   double Lloc = Md - 1.0;
   {
     static_assert(kTauMaxBins == kTauThreads, "one bin per thread");
     const int bin = kTauMaxBins - 1 - tid;  // thread 0 owns the top bin
-    int tot;
     const int x = static_cast<int>(hist[bin]);
-    const int c = block_excl_scan<kTauThreads>(x, red_i, tot) + x;  // bins >= bin
+    // page maxima in bins >= bin: a scan in thread order
+    const int incl = wave_incl_scan_dpp(x);
+    if (lane == kWave - 1) s_wscan[wave] = incl;
+    lds_barrier();
+    int c = incl;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c += (w < wave) ? s_wscan[w] : 0;
     if (c > 0) {
       const double edge = (Md - 1.0) + static_cast<double>(bin) / kTauMaxBins;
       const double kk = static_cast<double>(c);
@@ -296,9 +318,17 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       Lloc = fmax(Lloc, edge - drop);
     }
   }
-  double L = block_max_d<kTauThreads>(Lloc, red_d);
+  Lloc = wave_max_d(Lloc);
+  if (lane == 0) s_wL[wave] = Lloc;
+  lds_barrier();
+  double L = s_wL[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) L = fmax(L, s_wL[w]);
   // Snap down to a multiple of 2^-24 so that z - L is exact in double.
   L = floor(L * 16777216.0) / 16777216.0;
+  // For a float z, z > L exactly when z > Lf, the largest float <= L.
+  float Lf = static_cast<float>(L);
+  if (static_cast<double>(Lf) > L) Lf = nextafterf(Lf, -INFINITY);
 
   // Pages whose maximum exceeds L: each wave lists those of its 64-page
   // tiles (in page order within the wave), then the lists are laid end to
@@ -306,7 +336,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   int npw = 0;
   const unsigned long long below = (1ull << lane) - 1ull;
   auto list_page = [&](int j, float v) {  // called by whole waves
-    const bool flag = j < cnt && static_cast<double>(v) > L;
+    const bool flag = j < cnt && v > Lf;
     const unsigned long long ball = __ballot(flag);
     const int rk = npw + __popcll(ball & below);
     if (flag && rk < SEGP) cpages[wave][rk] = j;
@@ -314,8 +344,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   };
 #pragma unroll
   for (int k = 0; k < U4; ++k)
+    if (k < nsl)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) list_page(page_k(k, e), pv[4 * k + e]);
+      for (int e = 0; e < 4; ++e) list_page(page_k(k, e), pv[4 * k + e]);
   for (int jb = CACHED + wave * kWave; jb < cnt; jb += kTauThreads) {
     const int j = jb + lane;
     list_page(j, j < cnt ? pm[j] : -FLT_MAX);
@@ -359,7 +390,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         zs[k] = 0;
         if (jj < n_pg) {
           const int j = page_of(jj);
-          if (listed || static_cast<double>(pm[j]) > L)
+          if (listed || pm[j] > Lf)
             zv[k] = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(j) * P + t4);
           // the page's pool slot (written by the score pass), for the
           // value gather at the end; loaded alongside the scores
@@ -372,7 +403,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         const float ze[4] = {zv[k].x, zv[k].y, zv[k].z, zv[k].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool hit = static_cast<double>(ze[e]) > L;
+          const bool hit = ze[e] > Lf;
           const unsigned long long ball = __ballot(hit);
           const int sidx = nc + __popcll(ball & below);
           if (hit && sidx < CSEG) {
@@ -400,9 +431,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       for (int fi = tid; fi < span; fi += kTauThreads) {
         const int jj = fi / P, t = fi - jj * P;
         const int j = page_of(jj);
-        if (!listed && !(static_cast<double>(pm[j]) > L)) continue;
+        if (!listed && !(pm[j] > Lf)) continue;
         const float z = zh[static_cast<size_t>(j) * P + t];
-        if (static_cast<double>(z) > L) fn(z);
+        if (z > Lf) fn(z);
       }
     }
   };
@@ -411,21 +442,6 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   bool solved = false;
   double blo = L, bhi = Md;  // bracket for the fallback
 
-  // Exact solve by support iteration (r in {1, 2}, candidates staged), by
-  // the whole block.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
-  // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
-  // over S(t) = {y > t}, the count K, sum y and sum y^2, and finds min_S y.
-  // The closed form t* of tau for the support S (sparsemax: (sum y - 1)/K;
-  // 1.5-entmax: the smaller root of sum_S (y - t)^2 = 1) is tau itself when
-  // t* < min_S y, since then S(t*) = S.  Otherwise t moves up: for r = 1 to
-  // t* (over a superset of the support the terms below tau are negative, so
-  // t* <= tau: Michelot's iteration), for r = 2 by a Newton step on
-  // F^(1/2) - 1 (convex, so the step stays below tau).  Each wave reduces
-  // its threads' sums in a fixed pattern and the wave totals are added in
-  // wave order, so every thread takes the same steps and the result is the
-  // same on every run.  One barrier per pass; the wave totals alternate
-  // between two LDS rows so that a pass never overwrites totals still being
-  // read.
   // Exact solve by support iteration (r in {1, 2}, candidates staged), by
   // wave 0 alone.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
   // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
@@ -452,20 +468,25 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         segs[w + 1] = segs[w] + __builtin_amdgcn_readfirstlane(s_ccnt[w]);
       const int n_all = segs[NW];
       const bool in_regs = n_all <= R * kWave;
+      // register slots in use (uniform); the others are never visited
+      const int nslot = min(R, (n_all + kWave - 1) / kWave);
+      // (the loads are unconditional, from a clamped index, so that they
+      // are all in flight together)
       float yr[R];
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const int e = lane + k * kWave;
-        yr[k] = -INFINITY;
-        if (in_regs && e < n_all) {
-          int base = 0, w = 0;
+        int base = 0, w = 0;
 #pragma unroll
-          for (int v = 1; v < NW; ++v)
-            if (e >= segs[v]) { w = v; base = segs[v]; }
-          yr[k] = cand[w * CSEG + (e - base)];
-        }
+        for (int v = 1; v < NW; ++v)
+          if (e >= segs[v]) { w = v; base = segs[v]; }
+        const bool on = in_regs && e < n_all;
+        const float zc = cand[on ? w * CSEG + (e - base) : 0];
+        yr[k] = on ? zc : -INFINITY;
       }
-      double t = L - Md, res = 0.0;
+
+      double t = L - Md;
+      double res = 0.0;
       bool ok = false;
       for (int it = 0; it < kTauIters; ++it) {
         int K = 0;
@@ -482,7 +503,8 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         };
         if (in_regs) {
 #pragma unroll
-          for (int k = 0; k < R; ++k) visit(yr[k]);
+          for (int k = 0; k < R; ++k)
+            if (k < nslot) visit(yr[k]);
         } else {
           for (int w = 0; w < NW; ++w)
             for (int i = lane; i < s_ccnt[w]; i += kWave) visit(cand[w * CSEG + i]);
@@ -693,16 +715,18 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     if (tau_user) tau_user[ug] = tau;
   }
 
-  // Weighted value sum over the support, when every candidate is staged
-  // (the support, z > tau, is among them): p = max(z - tau, 0)^r as in the
+  // Weighted value sum over the support, p = max(z - tau, 0)^r as in the
   // chunked path, value rows gathered through the page table.  Each wave
-  // compacts its own segment in place to (p, position) of the support, then
-  // reads its rows with D/8 lanes per row and many rows in flight.  Sums run
-  // in a fixed order, so the result is the same on every run.  Heads done
-  // here are skipped by the apply step, whose per-unit chunk counter is
-  // reset here for it.
+  // compacts (p, position) of support tokens into its own LDS segment and
+  // reads their rows with D/8 lanes per row and many rows in flight.  When
+  // every candidate is staged the support is among them and is compacted in
+  // place; otherwise, with a selection, the wave walks its share of the
+  // kept pages again and gathers whenever its segment fills.  Sums run in a
+  // fixed order, so the result is the same on every run.  Only the full
+  // cache (no selection) leaves such heads to the apply step, whose per-unit
+  // chunk counter is reset here for it.
   if (tid == 0 && ug % G == 0) ctr[u] = 0;
-  if (!staged) {
+  if (!staged && sel == nullptr) {
     if (tid == 0) {
       done[ug] = 0;
       atomicAdd(undone, 1);
@@ -712,55 +736,105 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   constexpr int LPT = D / 8, TPW = kWave / LPT, RU = 8;
   const int h = u % H;
   const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
-  int nk = 0;
-  {
+  float *seg_p = cand + wave * CSEG;
+  int *seg_pos = cpos + wave * CSEG;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  float psum = 0.f;
+  // adds sum p v over entries [0, n) of the wave's segment
+  auto gather = [&](int n) {
+    for (int base = 0; base < n; base += TPW * RU) {
+      float x[RU][8];
+      float pw[RU];
+#pragma unroll
+      for (int rr = 0; rr < RU; ++rr) {
+        const int k = base + rr * TPW + sub;
+        pw[rr] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[rr][j] = 0.f;
+        if (k < n) {
+          pw[rr] = seg_p[k];
+          const int pos = seg_pos[k];
+          const int jj = pos >> lgP, t = pos & (P - 1);
+          const int slot =
+              listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
+          load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RU; ++rr) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(pw[rr], x[rr][j], acc[j]);
+        if (li == 0) psum += pw[rr];
+      }
+    }
+  };
+  if (staged) {
+    int nk = 0;
     const int nc = s_ccnt[wave];
     for (int i0 = 0; i0 < nc; i0 += kWave) {
       const int i = i0 + lane;
       float pv = 0.f;
       int pos = 0;
       if (i < nc) {
-        pv = pow_r(fmaxf(cand[wave * CSEG + i] - tau, 0.f), r, rg);
-        pos = cpos[wave * CSEG + i];
+        pv = pow_r(fmaxf(seg_p[i] - tau, 0.f), r, rg);
+        pos = seg_pos[i];
       }
       const bool keep = pv > 0.f;
       const unsigned long long ball = __ballot(keep);
       if (keep) {
         const int k = nk + __popcll(ball & below);
-        cand[wave * CSEG + k] = pv;  // k <= i: written after this chunk's reads
-        cpos[wave * CSEG + k] = pos;
+        seg_p[k] = pv;  // k <= i: written after this chunk's reads
+        seg_pos[k] = pos;
       }
       nk += __popcll(ball);
     }
-  }
-  float acc[8];
+    gather(nk);
+  } else {
+    // Steps of 4 kWave / P listed pages (4 scores per lane), dealt to the
+    // waves in turn, US at a time; a step adds at most 4 kWave entries.
+    constexpr int US = 2;
+    static_assert(CSEG >= 2 * US * 4 * kWave, "segment holds two passes");
+    const int lpp = P / 4, ppw = kWave / lpp;
+    const int sp = lane / lpp, t4 = 4 * (lane - sp * lpp);
+    const int steps = (n_pg + ppw - 1) / ppw;
+    int nk = 0;
+    for (int s0 = wave; s0 < steps; s0 += NW * US) {
+      float4 zv[US];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  float psum = 0.f;
-  for (int base = 0; base < nk; base += TPW * RU) {
-    float x[RU][8];
-    float pw[RU];
+      for (int k = 0; k < US; ++k) {
+        const int jj = (s0 + k * NW) * ppw + sp;
+        zv[k] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (jj < n_pg) {
+          const int j = page_of(jj);
+          if (pm[j] > tau)
+            zv[k] = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(j) * P + t4);
+        }
+      }
 #pragma unroll
-    for (int rr = 0; rr < RU; ++rr) {
-      const int k = base + rr * TPW + sub;
-      pw[rr] = 0.f;
+      for (int k = 0; k < US; ++k) {
+        const int jj = (s0 + k * NW) * ppw + sp;
+        const float ze[4] = {zv[k].x, zv[k].y, zv[k].z, zv[k].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[rr][j] = 0.f;
-      if (k < nk) {
-        pw[rr] = cand[wave * CSEG + k];
-        const int pos = cpos[wave * CSEG + k];
-        const int jj = pos >> lgP, t = pos & (P - 1);
-        const int slot =
-            listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
-        load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
+        for (int e = 0; e < 4; ++e) {
+          const float pv = pow_r(fmaxf(ze[e] - tau, 0.f), r, rg);
+          const bool keep = pv > 0.f;
+          const unsigned long long ball = __ballot(keep);
+          if (keep) {
+            const int kk = nk + __popcll(ball & below);
+            seg_p[kk] = pv;
+            seg_pos[kk] = jj * P + t4 + e;
+          }
+          nk += __popcll(ball);
+        }
+      }
+      if (nk > CSEG - US * 4 * kWave) {  // uniform
+        gather(nk);
+        nk = 0;
       }
     }
-#pragma unroll
-    for (int rr = 0; rr < RU; ++rr) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(pw[rr], x[rr][j], acc[j]);
-      if (li == 0) psum += pw[rr];
-    }
+    gather(nk);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -1587,6 +1661,8 @@ hipError_t launch_entmax_apply(const ekv_paged_kv &kv, float alpha,
                                const int32_t *sel, const int32_t *count,
                                float *out, float *probs, void *ws,
                                hipStream_t stream) {
+  // With a selection the threshold step has written every row of out.
+  if (sel && !probs) return hipSuccess;
   const DecodeWs L = decode_ws_layout(kv);
   char *w = static_cast<char *>(ws);
   const int mc = max_chunks(kv);

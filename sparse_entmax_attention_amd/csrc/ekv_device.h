@@ -212,6 +212,45 @@ __device__ __forceinline__ float wave_min_f(float x) {
   x = fminf(x, __int_as_float(dpp_rows<kDppRowBcast31, 0xC>(__float_as_int(x), idle)));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
 }
+// For maxima a lane of a row the broadcast skips keeps its own value.
+__device__ __forceinline__ float wave_max_f(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, __int_as_float(dpp_rows<kDppRowBcast15, 0xA>(__float_as_int(x),
+                                                            __float_as_int(x))));
+  x = fmaxf(x, __int_as_float(dpp_rows<kDppRowBcast31, 0xC>(__float_as_int(x),
+                                                            __float_as_int(x))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_rows_keep_d(double x) {
+  const unsigned long long v = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = dpp_rows<CTRL, ROWS>(static_cast<int>(v), static_cast<int>(v));
+  const int hi = dpp_rows<CTRL, ROWS>(static_cast<int>(v >> 32), static_cast<int>(v >> 32));
+  return __longlong_as_double(static_cast<long long>(
+      (static_cast<unsigned long long>(static_cast<unsigned int>(hi)) << 32) |
+      static_cast<unsigned int>(lo)));
+}
+__device__ __forceinline__ double wave_max_d(double x) {
+  x = fmax(x, dpp_d<kDppRowMirror>(x));
+  x = fmax(x, dpp_d<kDppRowHalfMirror>(x));
+  x = fmax(x, dpp_d<kDppQuad2301>(x));
+  x = fmax(x, dpp_d<kDppQuad1032>(x));
+  x = fmax(x, dpp_rows_keep_d<kDppRowBcast15, 0xA>(x));
+  x = fmax(x, dpp_rows_keep_d<kDppRowBcast31, 0xC>(x));
+  return readlane_d(x, kWave - 1);
+}
+// Inclusive prefix sum over the wave without LDS: within each 16-lane row
+// by shifts of 1, 2, 4 and 8 lanes (a lane with no source adds 0), then the
+// row totals carried into the later rows by the two row broadcasts.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += dpp_rows<kDppRowBcast15, 0xA>(x, 0);
+  x += dpp_rows<kDppRowBcast31, 0xC>(x, 0);
+  return x;
+}
 
 // Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
 // it does not wait for outstanding global loads, so loads issued before it

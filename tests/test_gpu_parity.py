@@ -358,3 +358,51 @@ def test_topk_ties_across_tiles(gpu):
         want = list(O.select_topk(gmax, k))
         assert int(buf.count[0, h]) == k
         assert list(buf.sel[0, h, :k].cpu().numpy()) == want
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_selection_with_candidates_beyond_lds(gpu, alpha):
+    # Keys of tiny magnitude put the scores of all 12,779 tokens within a few
+    # thousandths of each other, inside the threshold bracket, so a head's
+    # candidate scores do not fit on chip (8192 per head): with a selection the
+    # threshold step walks the kept pages again to gather the support's
+    # values, and the full cache leaves those heads to the apply step.  Both
+    # must match the oracle.
+    D, P, npg, H, G = 128, 64, 200, 2, 4
+    n = npg * P - 21
+    print("[case] candidates beyond LDS, alpha %g" % alpha, flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(31)
+    k = (3e-4 * torch.randn(npg, H, P, D, generator=g)).to(torch.bfloat16).to(gpu)
+    v = torch.randn(npg, H, P, D, generator=g).to(torch.bfloat16).to(gpu)
+    pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
+    sl = torch.tensor([n], dtype=torch.int32, device=gpu)
+    q = torch.randn(1, H * G, D, generator=g).to(gpu)
+    kv = ekv.PagedKV(k, v, pt, sl, G)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_topk(q, alpha, npg)
+    torch.cuda.synchronize()
+    assert (buf.count == npg).all()
+    sel_tau, sel_out = f64(buf.tau), f64(buf.out)
+    buf.entmax(q, alpha, selected=False)
+    torch.cuda.synchronize()
+    full_tau, full_out = f64(buf.tau), f64(buf.out)
+    kh, vh, qh = f64(k), f64(v), f64(q)
+    rows = pt.cpu().numpy()[0]
+    sc, r = 1 / math.sqrt(D), 1 / (alpha - 1)
+    for h in range(H):
+        keys = kh[rows, h].reshape(-1, D)[:n]
+        vals = vh[rows, h].reshape(-1, D)[:n]
+        for j in range(G):
+            hq = h * G + j
+            z = (alpha - 1) * O.token_scores(qh[0, hq], keys, sc)
+            # every page maximum lies within npg^(-1/r) of the largest
+            # score, so the bracket's lower end is at most max z - npg^(-1/r)
+            assert (z > z.max() - npg ** (-1 / r)).sum() > 8192
+            t = O.entmax_threshold(z, alpha)
+            p = O.entmax_probs(z, t, alpha)
+            o = (p[:, None] * vals).sum(0)
+            for tau_, out_ in ((sel_tau, sel_out), (full_tau, full_out)):
+                assert abs(tau_[0, hq] - t) <= TAU_ATOL, (h, j)
+                assert rel_l2(out_[0, hq], o) <= OUT_RTOL_L2, (h, j)
