@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     gauss_term(e.x, last ? -1.0f - e.y : e.y,
                last ? last_n : static_cast<float>(P), t, r, f, df);
   };
-  float tau = tau_lo;
+  float tau = tau_lo, prev_step = INFINITY;
   for (int it = 0; it < 64; ++it) {
     float f = 0.f, df = 0.f;
     for (int i = wave; i < n_st; i += kGtWaves) page_terms(i, tau, f, df);
@@ -536,7 +536,18 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     }
     float next;
     if (!step_from(ff, dd, tau, next)) break;
+    // In the quadratic phase of the iteration a step s that is rho times
+    // the one before is followed by one of about rho^2 s.  With s below
+    // 1e-4 max(1, |tau|) and rho below 0.01 that is about 1e-8 (relative),
+    // under float rounding, so the iteration ends here rather than spend a
+    // pass confirming it.  (A small step alone would not do: from below, a
+    // convex F's Newton step falls short of the distance to the root where
+    // F flattens out; a sharp drop in the step shows that it does not.)
+    const float step = next - tau;
+    const bool last = step <= 1e-4f * fmaxf(1.0f, fabsf(tau)) && step <= 0.01f * prev_step;
+    prev_step = step;
     tau = next;
+    if (last) break;
   }
   if (tid == 0) tau_hat[row] = tau;
 
