@@ -38,6 +38,11 @@ Pinning (see tests/test_oracle_*.py):
     readings of the summary's Gaussian selector paragraph; no page fixes
     them numerically.  Limits (Delta -> inf keeps every page) are pinned.
   * softmax_attend: pinned (shift invariance, alpha -> 1 limit of entmax).
+  * dropped_mass, softmax_dropped_mass, support_recall,
+    matched_budget_quality: pinned (covering sets give zero dropped mass,
+    full recall and the full-cache output; the softmax mass outside a set
+    equals 1 - exp(lse(kept) - lse(all)); the output error stays within
+    2 B delta).
 """
 from __future__ import annotations
 
@@ -53,6 +58,7 @@ __all__ = [
     "page_max_estimate", "gauss_keep", "entmax_threshold",
     "entmax_threshold_bisect", "entmax_probs", "entmax_attend",
     "softmax_attend", "pages_to_tokens", "decode_unit", "dropped_mass",
+    "softmax_dropped_mass", "support_recall", "matched_budget_quality",
 ]
 
 
@@ -486,3 +492,57 @@ def dropped_mass(q: np.ndarray, keys: np.ndarray, kept_tokens, scale: float,
     mask = np.ones(len(z), dtype=bool)
     mask[np.asarray(kept_tokens, dtype=np.int64)] = False
     return float(p[mask].sum()), p, tau
+
+
+def softmax_dropped_mass(q: np.ndarray, keys: np.ndarray, kept_tokens,
+                         scale: float) -> float:
+    """Full-cache softmax mass of the tokens outside a kept set, summed
+    directly from the normalised weights (softmax gives every token weight,
+    so this is zero only when every token is kept)."""
+    s = token_scores(q, keys, scale)
+    w = np.exp(s - np.max(s))
+    w /= np.sum(w)
+    mask = np.ones(len(s), dtype=bool)
+    mask[np.asarray(kept_tokens, dtype=np.int64)] = False
+    return float(w[mask].sum())
+
+
+def support_recall(p_full: np.ndarray, kept_tokens) -> float:
+    """Share of the full-cache entmax support (p_i > 0) inside a kept set."""
+    support = np.flatnonzero(np.asarray(p_full) > 0.0)
+    kept = np.zeros(len(p_full), dtype=bool)
+    kept[np.asarray(kept_tokens, dtype=np.int64)] = True
+    return float(kept[support].sum()) / max(len(support), 1)
+
+
+def matched_budget_quality(qs: np.ndarray, keys: np.ndarray, vals: np.ndarray,
+                           P: int, scale: float, alpha: float, pages) -> dict:
+    """Entmax against softmax on one kept page set (the same budget for both).
+
+    Per query head of qs [G][D]: the full-cache mass each distribution puts
+    outside the kept tokens (delta_entmax, delta_softmax), the share of the
+    entmax support inside them (recall), and the relative L2 error of the
+    output computed on the kept tokens alone against the full-cache output
+    (err_entmax, err_softmax).  The Technical Summary (§3) bounds the entmax
+    error by 2 B delta and notes that it vanishes when the kept set covers
+    the support; softmax weights never vanish, so its mass outside any
+    proper subset is positive.
+    """
+    N = keys.shape[0]
+    toks = pages_to_tokens(pages, N, P)
+    out = {k: [] for k in ("delta_entmax", "delta_softmax", "recall",
+                           "err_entmax", "err_softmax")}
+    for q in qs:
+        de, p_full, _ = dropped_mass(q, keys, toks, scale, alpha)
+        o_full = p_full @ vals
+        o_kept, _, _ = entmax_attend(q, keys[toks], vals[toks], scale, alpha)
+        so_full, _ = softmax_attend(q, keys, vals, scale)
+        so_kept, _ = softmax_attend(q, keys[toks], vals[toks], scale)
+        out["delta_entmax"].append(de)
+        out["delta_softmax"].append(softmax_dropped_mass(q, keys, toks, scale))
+        out["recall"].append(support_recall(p_full, toks))
+        out["err_entmax"].append(float(np.linalg.norm(o_kept - o_full) /
+                                       np.linalg.norm(o_full)))
+        out["err_softmax"].append(float(np.linalg.norm(so_kept - so_full) /
+                                        np.linalg.norm(so_full)))
+    return {k: np.array(v) for k, v in out.items()}

@@ -187,3 +187,69 @@ def test_support_recovery_is_exact_and_error_bound_holds():
             if delta > 0:
                 worst = max(worst, err / (2 * Bv * delta))
         assert worst > 0.0
+
+
+def test_softmax_dropped_mass_two_tokens():
+    # scores 0 and ln 3 (scale 1, unit vectors): weights 1/4 and 3/4
+    K = np.array([[0.0, 0.0], [math.log(3.0), 0.0]])
+    q = np.array([1.0, 0.0])
+    assert abs(O.softmax_dropped_mass(q, K, [0], 1.0) - 0.75) < 1e-15
+    assert abs(O.softmax_dropped_mass(q, K, [1], 1.0) - 0.25) < 1e-15
+    assert O.softmax_dropped_mass(q, K, [0, 1], 1.0) == 0.0
+
+
+def test_softmax_dropped_mass_equals_lse_gap():
+    # mass outside = 1 - exp(lse(kept) - lse(all)), two independent routes
+    rng = np.random.default_rng(41)
+    K = rng.normal(size=(500, 32))
+    V = rng.normal(size=(500, 32))
+    for _ in range(20):
+        q = rng.normal(size=32) * 2.0
+        kept = np.sort(rng.choice(500, int(rng.integers(1, 500)), replace=False))
+        _, l_all = O.softmax_attend(q, K, V, 0.3)
+        _, l_kept = O.softmax_attend(q, K[kept], V[kept], 0.3)
+        d = O.softmax_dropped_mass(q, K, kept, 0.3)
+        assert abs(d - (1.0 - math.exp(l_kept - l_all))) < 1e-12
+
+
+def test_support_recall_cases():
+    p = np.array([0.0, 0.5, 0.0, 0.3, 0.2, 0.0])
+    assert O.support_recall(p, [1, 3, 4]) == 1.0
+    assert O.support_recall(p, [0, 2, 5]) == 0.0
+    assert abs(O.support_recall(p, [1, 2]) - 1.0 / 3.0) < 1e-15
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_matched_budget_quality(alpha):
+    rng = np.random.default_rng(43)
+    P, N, D = 16, 16 * 40 - 5, 16
+    K = rng.normal(size=(N, D))
+    K[100:140] += 2.0 * rng.normal(size=D)  # one page run the queries align with
+    V = rng.normal(size=(N, D))
+    qs = np.stack([K[120] * 0.05, K[130] * 0.05])  # supports over pages 6-8
+    sc = 0.5
+    # every page: nothing dropped, the full-cache outputs
+    allp = np.arange((N + P - 1) // P)
+    m = O.matched_budget_quality(qs, K, V, P, sc, alpha, allp)
+    assert (m["delta_entmax"] == 0).all() and (m["delta_softmax"] == 0).all()
+    assert (m["recall"] == 1).all()
+    assert (m["err_entmax"] < 1e-12).all() and (m["err_softmax"] < 1e-12).all()
+    # the pages holding each head's support: entmax exact, softmax not
+    supp_pages = set()
+    for q in qs:
+        _, p, _ = O.dropped_mass(q, K, [], sc, alpha)
+        supp_pages |= set((np.flatnonzero(p > 0) // P).tolist())
+    pages = np.array(sorted(supp_pages))
+    assert len(pages) < len(allp)
+    m = O.matched_budget_quality(qs, K, V, P, sc, alpha, pages)
+    assert (m["delta_entmax"] == 0).all() and (m["recall"] == 1).all()
+    assert (m["err_entmax"] < 1e-12).all()
+    assert (m["delta_softmax"] > 0).all() and (m["err_softmax"] > 0).all()
+    # a set missing part of the support: error within 2 B delta
+    Bv = np.linalg.norm(V, axis=1).max()
+    m = O.matched_budget_quality(qs, K, V, P, sc, alpha, pages[: len(pages) // 2])
+    for h, q in enumerate(qs):
+        _, p, _ = O.dropped_mass(q, K, [], sc, alpha)
+        o_full = p @ V
+        assert m["delta_entmax"][h] > 0 and m["recall"][h] < 1
+        assert m["err_entmax"][h] * np.linalg.norm(o_full) <= 2 * Bv * m["delta_entmax"][h] + 1e-12
