@@ -151,6 +151,7 @@ def main():
 
     import sparse_entmax_attention_amd as ekv
     import workloads
+    from sparse_entmax_attention_amd.quality import matched_budget_quality
 
     dev = torch.device("cuda:0")
     spec = workloads.workload(args.workload)
@@ -328,6 +329,13 @@ def main():
         r = run_leg(name, steps, warm)
         if name in ("gauss", "topk"):
             pages, toks = selection_stats()
+            # what the selection costs each attention (same pages for both),
+            # measured after the timed steps from the selection they left
+            qm = matched_budget_quality(buf, q, alpha)
+            r["quality"] = {k: {"mean": round(v.mean().item(), 6),
+                                "min": round(v.min().item(), 6),
+                                "max": round(v.max().item(), 6)}
+                            for k, v in qm.items()}
             rows = support_rows(True)
             kbytes = toks * D * e
             vbytes = rows * D * e
