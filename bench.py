@@ -134,6 +134,12 @@ def parse():
                     help="(sequence, KV head) units the oracle is timed on; "
                          "-1 (default) all units of one step, 0 skips")
     ap.add_argument("--legs", default="gauss,topk,entmax_full,softmax_full")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: time the top-k and "
+                         "Gaussian steps on prefixes of the workload's "
+                         "sequences (16k tokens up to their full length) and "
+                         "print one JSON line with the selection and step "
+                         "times per length")
     return ap.parse_args()
 
 
@@ -319,6 +325,49 @@ def main():
     meta_gauss_bytes = n_pages_total * H * 2 * D * 4
     meta_bbox_bytes = n_pages_total * H * 2 * D * e
     tail_bytes = B * H * (P * D * e)
+
+    if args.sweep:
+        # Prefixes of every sequence, multiples of the page size, so that the
+        # metadata built for the whole cache is that of each prefix.
+        full_lens = list(inp.lens)
+        lengths = [L for L in (1 << 14, 1 << 15, 1 << 16, 1 << 17, 1 << 18,
+                               1 << 19, 1 << 20) if L <= max(full_lens)]
+        rows = []
+        for L in lengths:
+            lens = [min(L, n) for n in full_lens]
+            inp.lens[:] = lens
+            inp.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+            tail.copy_(torch.tensor([(n - 1) // P for n in lens], dtype=torch.int32))
+            n_pages = sum((n + P - 1) // P for n in lens)
+            row = {"seq_len": L}
+            for name, sel_phases in (("topk", ("meta_tail", "score_bbox", "select_topk")),
+                                     ("gauss", ("score_gauss", "select_gauss"))):
+                r = run_leg(name, args.steps, args.warmup)
+                pages, toks = selection_stats()
+                meta = n_pages * H * 2 * D * (4 if name == "gauss" else e)
+                row[name] = {
+                    "step_us": round(r["median_ms"] * 1e3, 2),
+                    "select_us": round(sum(r["phase_ms"][k] for k in sel_phases) * 1e3, 2),
+                    "selected_pages": pages,
+                    "phase_us": {k: round(v * 1e3, 2) for k, v in r["phase_ms"].items()},
+                    "metadata_bytes": meta,
+                    "selected_k_bytes": toks * D * e,
+                }
+            log("[sweep] %7d tokens: top-k select %.1f us, step %.1f us | "
+                "gauss select %.1f us, step %.1f us (%d pages kept)" % (
+                    L, row["topk"]["select_us"], row["topk"]["step_us"],
+                    row["gauss"]["select_us"], row["gauss"]["step_us"],
+                    row["gauss"]["selected_pages"]))
+            rows.append(row)
+        print(json.dumps({"sweep": rows, "workload": spec.name, "batch": B,
+                          "kv_heads": H, "group": G, "head_dim": D, "page_size": P,
+                          "alpha": alpha, "delta": delta, "topk": k_top,
+                          "steps": args.steps, "warmup": args.warmup,
+                          "note": "select_us sums the per-phase event times "
+                                  "(scoring with the tail refresh, selection); "
+                                  "step_us is the headline pass of the whole step"}),
+              flush=True)
+        return
 
     results = {}
     wanted = [x for x in args.legs.split(",") if x]
