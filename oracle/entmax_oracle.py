@@ -30,7 +30,10 @@ Pinning (see tests/test_oracle_*.py):
   * gauss_moments: pinned (exact variance of the score of a page's tokens
     in the single-coordinate case; Monte Carlo).
   * select_topk: pinned (brute force over subsets, nesting, k >= n).
-  * gauss_excess_moment: pinned (numerical quadrature, Monte Carlo).
+  * gauss_excess_moment, excess_standard: pinned (numerical quadrature of
+    the defining integral for r in {1, 2, 4/3, 3, 4, 7.5} on both sides of
+    the series switch, the closed forms at r = 1 and 2, the recurrence
+    J_r = (r-1) J_(r-2) - c J_(r-1), Monte Carlo).
   * solve_tau_hat: pinned (zero-variance limit equals the exact entmax
     threshold of the repeated means; monotonicity; uniqueness).
   * gauss_keep: parity unpinned beyond self-consistency.  The estimated
@@ -54,7 +57,8 @@ from scipy import special as _sp
 __all__ = [
     "bf16_bits_to_f64", "unit_tokens", "page_token_counts", "page_metadata",
     "unit_metadata", "token_scores", "bbox_bound", "gauss_moments",
-    "select_topk", "gauss_excess_moment", "gauss_normaliser", "solve_tau_hat",
+    "select_topk", "excess_standard", "gauss_excess_moment",
+    "gauss_normaliser", "solve_tau_hat",
     "page_max_estimate", "gauss_keep", "entmax_threshold",
     "entmax_threshold_bisect", "entmax_probs", "entmax_attend",
     "softmax_attend", "pages_to_tokens", "decode_unit", "dropped_mass",
@@ -213,15 +217,45 @@ def _Phi(c):
     return 0.5 * _sp.erfc(-c / math.sqrt(2.0))
 
 
-def gauss_excess_moment(m, s, tau, r: int):
-    """E[max(Z - tau, 0)^r] for Z ~ N(m, s^2), r in {1, 2}.
+def excess_standard(c, r: float):
+    """J_r(c) = E[max(X - c, 0)^r] for X standard normal and real r >= 1.
+
+    J_r(c) = int_0^inf y^r phi(y + c) dy = phi(c) int_0^inf y^r e^(-c y - y^2/2) dy,
+    and the last integral is Gamma(r + 1) e^(c^2/4) D_(-r-1)(c) with D the
+    parabolic cylinder function (its standard integral representation), so
+    J_r(c) = Gamma(r + 1) e^(-c^2/4) D_(-r-1)(c) / sqrt(2 pi).  Far below the
+    mean (c < -30), where D overflows in double, X - c = a (1 + X/a) with
+    a = -c and the expectation is the series sum_k C(r, 2k) (2k-1)!! a^(r-2k)
+    (odd moments vanish; the mass where 1 + X/a < 0 is below 1e-190).
+    """
+    c = np.asarray(c, dtype=np.float64)
+    out = np.empty(c.shape)
+    far = c < -30.0
+    near = ~far
+    if np.any(near):
+        d, _ = _sp.pbdv(-r - 1.0, c[near])
+        out[near] = (_sp.gamma(r + 1.0) * np.exp(-0.25 * c[near] ** 2) * d
+                     / math.sqrt(2.0 * math.pi))
+    if np.any(far):
+        a = -c[far]
+        tot = np.ones(a.shape)
+        dfact = 1.0
+        for k in range(1, 16):
+            dfact *= 2 * k - 1
+            tot += _sp.binom(r, 2 * k) * dfact * a ** (-2.0 * k)
+        out[far] = a ** r * tot
+    return out
+
+
+def gauss_excess_moment(m, s, tau, r: float):
+    """E[max(Z - tau, 0)^r] for Z ~ N(m, s^2), real r >= 1.
 
     Writing Z - tau = u + s X with u = m - tau and X standard normal, the
     positive part is non-zero for X > -u/s; integrating against the normal
     density gives, with c = u/s,
       r = 1:  u Phi(c) + s phi(c)
       r = 2:  (u^2 + s^2) Phi(c) + u s phi(c)
-    and max(u, 0)^r when s = 0.
+    otherwise s^r J_r(-c) (excess_standard), and max(u, 0)^r when s = 0.
     """
     m = np.asarray(m, dtype=np.float64)
     s = np.asarray(s, dtype=np.float64)
@@ -240,7 +274,7 @@ def gauss_excess_moment(m, s, tau, r: int):
         elif r == 2:
             out[pos] = (uu * uu + ss * ss) * _Phi(c) + uu * ss * _phi(c)
         else:
-            raise ValueError("closed form only for r in {1, 2}")
+            out[pos] = ss ** r * excess_standard(-c, r)
     return out
 
 
@@ -264,7 +298,7 @@ def solve_tau_hat(mu: np.ndarray, sigma2: np.ndarray, n_tok: np.ndarray,
     tau_lo = max_p m_p - 1 Jensen's inequality gives F >= n_p* >= 1; the
     upper end doubles its distance from tau_lo until F <= 1.
     """
-    r = _integer_exponent(alpha)
+    r = _gauss_exponent(alpha)
     m = (alpha - 1.0) * np.asarray(mu, dtype=np.float64)
     s = (alpha - 1.0) * np.sqrt(np.maximum(np.asarray(sigma2, np.float64), 0))
     lo = float(np.max(m)) - 1.0
@@ -320,6 +354,17 @@ def gauss_keep(mu: np.ndarray, sigma2: np.ndarray, n_tok: np.ndarray,
 # ---------------------------------------------------------------------------
 # alpha-entmax  [Technical Summary, §2 and §2.C; arXiv abstract]
 # ---------------------------------------------------------------------------
+
+def _gauss_exponent(alpha: float) -> float:
+    """r = 1/(alpha - 1) for the Gaussian selector, which needs r >= 1
+    (alpha <= 2): then x -> max(x - tau, 0)^r is convex and the Jensen bound
+    and the monotone Newton iteration below hold.  Exactly 1 or 2 for
+    alpha = 2 or 1.5, so that the closed forms apply."""
+    if not (1.0 < alpha <= 2.0):
+        raise ValueError("the Gaussian selector needs 1 < alpha <= 2")
+    r = 1.0 / (alpha - 1.0)
+    return float(round(r)) if abs(r - round(r)) < 1e-12 else r
+
 
 def _integer_exponent(alpha: float) -> int:
     r = 1.0 / (alpha - 1.0)

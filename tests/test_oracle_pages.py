@@ -154,6 +154,89 @@ def test_gauss_excess_moment_monte_carlo_and_zero_variance():
         assert float(O.gauss_excess_moment(1.2, 0.0, 1.5, r)) == 0.0
 
 
+def _phi(c):
+    return math.exp(-0.5 * c * c) / math.sqrt(2 * math.pi)
+
+
+def _Q(c):
+    return 0.5 * math.erfc(c / math.sqrt(2))
+
+
+@pytest.mark.parametrize("c", [-45.0, -31.0, -29.0, -12.0, -3.0, -0.5, 0.0, 1.7, 6.0, 10.0])
+def test_excess_standard_matches_closed_forms(c):
+    # parabolic-cylinder form (and the series far below) against the
+    # elementary closed forms at r = 1, 2
+    j1 = _phi(c) - c * _Q(c)
+    j2 = (1 + c * c) * _Q(c) - c * _phi(c)
+    assert abs(float(O.excess_standard(c, 1.0)) - j1) <= 1e-11 * max(abs(j1), 1e-300)
+    assert abs(float(O.excess_standard(c, 2.0)) - j2) <= 1e-10 * max(abs(j2), 1e-300)
+
+
+@pytest.mark.parametrize("r", [4.0 / 3.0, 3.0, 4.0, 7.5])
+def test_excess_standard_quadrature(r):
+    # the defining integral J_r(c) = int_c^inf (x - c)^r phi(x) dx
+    for c in (-40.0, -31.0, -29.0, -10.0, -3.0, 0.0, 2.0, 6.0, 10.0):
+        f = lambda x: (x - c) ** r * _phi(x)
+        lo = max(c, -40.0)
+        val = sum(integrate.quad(f, a, b, limit=400, epsabs=0, epsrel=1e-13)[0]
+                  for a, b in ((lo, lo + 5), (lo + 5, max(lo + 5, 12.0) + 30)))
+        got = float(O.excess_standard(c, r))
+        assert abs(got - val) <= 1e-8 * val, (r, c, got, val)
+
+
+@pytest.mark.parametrize("r", [3.25, 4.5])
+def test_excess_standard_recurrence(r):
+    # integration by parts: J_r = (r - 1) J_(r-2) - c J_(r-1)
+    for c in (-20.0, -2.0, 0.0, 1.0, 4.0):
+        jr, j1, j2 = (float(O.excess_standard(c, x)) for x in (r, r - 1, r - 2))
+        assert abs(jr - ((r - 1) * j2 - c * j1)) <= 1e-9 * abs(jr)
+
+
+def test_gauss_excess_moment_general_r_monte_carlo():
+    rng = np.random.default_rng(19)
+    x = rng.normal(0.4, 0.9, 4_000_000)
+    for r in (4.0 / 3.0, 4.0):
+        mc = np.mean(np.maximum(x - 0.1, 0) ** r)
+        got = float(O.gauss_excess_moment(0.4, 0.9, 0.1, r))
+        assert abs(got - mc) < 5e-3 * mc
+        assert float(O.gauss_excess_moment(0.4, 0.0, 0.1, r)) == pytest.approx(0.3 ** r)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.75])
+def test_tau_hat_zero_variance_general_alpha(alpha):
+    # zero variance: the normalisation is the exact entmax one over the
+    # repeated page means (bisection threshold for these alpha)
+    rng = np.random.default_rng(11)
+    for _ in range(10):
+        n_pages = int(rng.integers(1, 30))
+        mu = rng.normal(0, 2, n_pages)
+        n_tok = rng.integers(1, 17, n_pages)
+        th = O.solve_tau_hat(mu, np.zeros(n_pages), n_tok, alpha)
+        z = np.repeat((alpha - 1) * mu, n_tok)
+        assert abs(th - O.entmax_threshold_bisect(z, alpha)) < 1e-9
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.75])
+def test_tau_hat_general_alpha_is_the_unique_root(alpha):
+    rng = np.random.default_rng(14)
+    r = 1 / (alpha - 1)
+    for _ in range(10):
+        n_pages = int(rng.integers(1, 150))
+        mu = rng.normal(0, 3, n_pages)
+        s2 = rng.uniform(0, 1.5, n_pages)
+        n_tok = np.full(n_pages, 32)
+        th = O.solve_tau_hat(mu, s2, n_tok, alpha)
+        m, s = (alpha - 1) * mu, (alpha - 1) * np.sqrt(s2)
+        assert abs(O.gauss_normaliser(th, m, s, n_tok, r) - 1.0) < 1e-9
+        assert O.gauss_normaliser(th - 1e-6, m, s, n_tok, r) > 1.0
+        assert O.gauss_normaliser(th + 1e-6, m, s, n_tok, r) < 1.0
+
+
+def test_solve_tau_hat_rejects_alpha_above_two():
+    with pytest.raises(ValueError):
+        O.solve_tau_hat(np.zeros(3), np.ones(3), np.full(3, 8), 2.5)
+
+
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_tau_hat_zero_variance_is_exact_threshold(alpha):
     # With zero page variance every token of page p scores mu_p, so the
