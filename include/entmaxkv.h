@@ -199,7 +199,12 @@ ekv_status ekv_select_topk(const ekv_paged_kv *kv, const float *ub, int32_t k,
  * threshold minus the margin).  If no page passes, the single page with the
  * largest margin max_h[(alpha-1) mhat_hp - tau_hat_h] is kept (lower index on
  * ties).  Outputs: sel/count as for top-k (ascending, count >= 1) and
- * tau_hat [batch][H_q] float32.  alpha must be 1.5 or 2 (r in {2, 1});
+ * tau_hat [batch][H_q] float32.  1.1 <= alpha <= 2 (r = 1/(alpha-1) in
+ * [1, 10], where x -> max(x - tau, 0)^r is convex): the expectation has a
+ * closed form in the normal CDF and density for alpha = 1.5 and 2 and is a
+ * 24-node Gauss-Jacobi sum (16-node Gauss-Hermite far below the page mean)
+ * otherwise, the rules built on the host at each call (see
+ * ekv_quadrature_rule); other alpha return EKV_ERR_UNSUPPORTED.
  * delta >= 0.  Workspace: ekv_workspace_size(EKV_OP_SELECT_GAUSS, kv, 0)
  * bytes (one 64-bit page mask per query head and 64-page tile), 256-byte
  * aligned; its contents on entry do not matter.  tau_hat is found by
@@ -290,6 +295,19 @@ ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
 #define EKV_READ_PROBE_SINK 8192
 ekv_status ekv_read_probe(const void *buf, size_t bytes, uint32_t *sink,
                           void *stream);
+
+/*
+ * ekv_quadrature_rule - the Gauss rules behind ekv_select_gauss at alpha
+ * other than 1.5 and 2 (host only; no device work).  kind 0: Gauss-Jacobi
+ * nodes and weights for the weight (1 + x)^param on [-1, 1], param > -1;
+ * kind 1: Gauss-Hermite for the standard normal density (param ignored).
+ * Writes n (1..64) nodes, ascending, and their weights to the host arrays
+ * nodes[n] and weights[n]; EKV_ERR_INVALID_ARG otherwise.
+ */
+#define EKV_RULE_JACOBI 0
+#define EKV_RULE_HERMITE 1
+ekv_status ekv_quadrature_rule(int32_t kind, double param, int32_t n,
+                               double *nodes, double *weights);
 
 /* Floats of the ub (EKV_SCORE_BBOX) or gstat (EKV_SCORE_GAUSS) buffer,
  * page values plus tile summaries (host only; 0 on invalid input). */

@@ -85,6 +85,9 @@ _SIGNATURES = {
                                      _c_i32]),
     "ekv_read_probe": (_c_i32, [_c_p, _c_size, _c_p, _c_p]),
     "ekv_score_size": (_c_size, [ctypes.POINTER(ekv_paged_kv), _c_i32]),
+    "ekv_quadrature_rule": (_c_i32, [_c_i32, ctypes.c_double, _c_i32,
+                                     ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double)]),
     "ekv_status_string": (ctypes.c_char_p, [_c_i32]),
     "ekv_last_error": (ctypes.c_char_p, []),
     "ekv_version": (_c_i32, []),
@@ -298,6 +301,21 @@ def ekv_read_probe(buf, sink, stream=None) -> None:
     _check(load_library().ekv_read_probe(
         _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
         _stream(stream)), "ekv_read_probe")
+
+
+EKV_RULE_JACOBI = 0
+EKV_RULE_HERMITE = 1
+
+
+def ekv_quadrature_rule(kind: int, param: float, n: int):
+    """Host-only: the (nodes, weights) lists of a Gauss rule used by the
+    Gaussian selector at general alpha (EKV_RULE_JACOBI: weight (1+x)^param
+    on [-1, 1]; EKV_RULE_HERMITE: the standard normal density)."""
+    x = (ctypes.c_double * n)()
+    w = (ctypes.c_double * n)()
+    _check(load_library().ekv_quadrature_rule(kind, float(param), n, x, w),
+           "ekv_quadrature_rule")
+    return list(x), list(w)
 
 
 def ekv_version() -> int:

@@ -9,6 +9,7 @@
 
 #include "ekv_device.h"
 #include "ekv_kernels.h"
+#include "gauss_rule.h"
 
 namespace {
 
@@ -261,9 +262,9 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
                             size_t ws_bytes, void *stream) {
   EKV_TRY(check_kv(kv, false, false));
   EKV_TRY(check_alpha(alpha));
-  if (alpha != 1.5f && alpha != 2.0f)
+  if (!(alpha >= 1.1f && alpha <= 2.0f))
     return fail(EKV_ERR_UNSUPPORTED,
-                "Gaussian selector built for alpha in {1.5, 2} (got %g)",
+                "Gaussian selector built for 1.1 <= alpha <= 2 (got %g)",
                 static_cast<double>(alpha));
   if (std::isnan(delta) || delta < 0.0f)
     return fail(EKV_ERR_INVALID_ARG, "delta must be >= 0 (got %g)",
@@ -370,6 +371,18 @@ ekv_status ekv_read_probe(const void *buf, size_t bytes, uint32_t *sink,
                 "buf (16-byte aligned), sink and a multiple of 16 bytes required");
   return hip_status(ekv::launch_read_probe(buf, bytes, sink, as_stream(stream)),
                     "ekv_read_probe launch");
+}
+
+ekv_status ekv_quadrature_rule(int32_t kind, double param, int32_t n,
+                               double *nodes, double *weights) {
+  if (!nodes || !weights || n < 1 || n > ekv::kMaxRuleNodes)
+    return fail(EKV_ERR_INVALID_ARG, "nodes, weights and 1 <= n <= %d required",
+                ekv::kMaxRuleNodes);
+  bool ok = false;
+  if (kind == EKV_RULE_JACOBI) ok = ekv::gauss_jacobi_rule(param, n, nodes, weights);
+  else if (kind == EKV_RULE_HERMITE) ok = ekv::gauss_hermite_rule(n, nodes, weights);
+  if (!ok) return fail(EKV_ERR_INVALID_ARG, "unknown rule kind or parameter out of range");
+  return EKV_OK;
 }
 
 const char *ekv_status_string(ekv_status s) {

@@ -14,6 +14,7 @@
 
 #include "ekv_device.h"
 #include "ekv_kernels.h"
+#include "gauss_rule.h"
 
 namespace ekv {
 
@@ -307,6 +308,59 @@ __device__ __forceinline__ void gauss_term(float m, float s, float n, float tau,
   }
 }
 
+// The same two terms at any r >= 1 (r code 0), from the Gauss rules in q.
+// With c = (tau - m)/s, E[(Z - tau)_+^r] = s^r J_r(c) for
+// J_r(c) = int_0^inf y^r phi(y + c) dy, and -dE/dtau = s^(r-1) K with
+// K = int_0^inf y^r (y + c) phi(y + c) dy (differentiating under the
+// integral).  Where c >= -6 both integrands are negligible past
+// y + c = 10, and y = h (1 + x), h = (10 - c)/2, turns them into
+// h^(r+1) times Gauss-Jacobi sums over x with weight (1 + x)^r of the
+// smooth factors phi(y + c) and (y + c) phi(y + c).  Further below the page
+// mean (c < -6), and for s = 0, the expectations are taken over Z directly
+// with the Gauss-Hermite rule: sum_i w_i (u + s x_i)_+^r and
+// r sum_i w_i (u + s x_i)_+^(r-1), u = m - tau (the nodes below -6 carry
+// under 1e-9 of the mass).
+__device__ __forceinline__ void gauss_term_rule(float m, float s, float n,
+                                                float tau, const GaussRule &q,
+                                                float &f, float &df) {
+  constexpr float kInvSqrt2Pi = 0.39894228040143268f;
+  constexpr float kHalfLog2e = 0.72134752044448170f;  // log2(e) / 2
+  const float u = m - tau;
+  const float r = q.r;
+  if (s > 0.f && u < 6.0f * s) {
+    const float c = -u * __builtin_amdgcn_rcpf(s);
+    const float h = 0.5f * (10.0f - c);
+    if (!(h > 0.f)) return;
+    float j = 0.f, k = 0.f;
+#pragma unroll
+    for (int i = 0; i < kJacobiNodes; ++i) {
+      const float t = fmaf(h, 1.0f + q.jx[i], c);  // y + c
+      const float e = q.jw[i] * __builtin_amdgcn_exp2f(-kHalfLog2e * t * t);
+      j += e;
+      k = fmaf(t, e, k);
+    }
+    // s^(r-1) h^(r+1) / sqrt(2 pi), in the log domain
+    const float sc = kInvSqrt2Pi * __builtin_amdgcn_exp2f(
+                                       (r - 1.0f) * __builtin_amdgcn_logf(s) +
+                                       (r + 1.0f) * __builtin_amdgcn_logf(h));
+    f = fmaf(n * sc * s, j, f);
+    df = fmaf(n * sc, k, df);
+  } else {
+    float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kHermiteNodes; ++i) {
+      const float v = fmaf(s, q.hx[i], u);
+      if (v > 0.f) {
+        const float pv = __builtin_amdgcn_exp2f((r - 1.0f) * __builtin_amdgcn_logf(v));
+        e1 = fmaf(q.hw[i], pv, e1);
+        e0 = fmaf(q.hw[i] * v, pv, e0);
+      }
+    }
+    f = fmaf(n, e0, f);
+    df = fmaf(n * r, e1, df);
+  }
+}
+
 // Exclusive prefix sums of L counters over a block of NT threads (thread
 // order) and their totals.  smem holds L * NT / 64 ints.  Contains barriers.
 template <int NT, int L>
@@ -335,11 +389,12 @@ __device__ __forceinline__ void block_scan_multi(const int (&x)[L], int (&pre)[L
   }
 }
 
-template <int G>
+template <int G, bool RULE>
 __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     const float *__restrict__ gstat, const int32_t *__restrict__ seq_lens,
     int batch, int H, int P, int max_pages, float am1, int r, float delta,
-    float *__restrict__ tau_hat, unsigned long long *__restrict__ masks) {
+    float *__restrict__ tau_hat, unsigned long long *__restrict__ masks,
+    const GaussRule rule) {
   __shared__ float2 s_sv[kGtSvItems * kPageTile];  // (m, s); s < 0: last page
   __shared__ float s_kz[kGtKzItems * kPageTile];
   __shared__ int s_slist[kGtListCap];
@@ -398,9 +453,13 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     M = fmaxf(M, s_red[0][w]);
     ML = fmaxf(ML, s_red[1][w]);
   }
-  const float inv_full = r == 2 ? rsqrtf(static_cast<float>(P))
-                                : 1.0f / static_cast<float>(P);
-  const float inv_last = r == 2 ? rsqrtf(last_n) : 1.0f / last_n;
+  // n^(-1/r) for the full and the last page (r code 0: rule.r)
+  auto inv_root = [&](float n) {
+    if constexpr (RULE) return __builtin_amdgcn_exp2f(-__builtin_amdgcn_logf(n) / rule.r);
+    return r == 2 ? rsqrtf(n) : 1.0f / n;
+  };
+  const float inv_full = inv_root(static_cast<float>(P));
+  const float inv_last = inv_root(last_n);
   const float tau_lo = fmaxf(am1 * M - inv_full, am1 * ML - inv_last);
   // Tile tests get a small margin: they only prune, the page tests decide.
   const float s_thr = tau_lo - 1e-5f * fmaxf(fabsf(tau_lo), 1.0f);
@@ -502,7 +561,10 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
   auto step_from = [&](float ff, float dd, float t, float &next) {
     if (!(ff > 1.0f) || !(dd > 0.0f)) return false;
     float step;
-    if (r == 2) {
+    if constexpr (RULE) {
+      // r F (1 - F^(-1/r)) / (-F'), with 1 - F^(-1/r) = -expm1(-ln F / r)
+      step = rule.r * ff * -expm1f(-logf(ff) / rule.r) / dd;
+    } else if (r == 2) {
       const float sf = sqrtf(ff);
       step = 2.0f * sf * (ff - 1.0f) / ((sf + 1.0f) * dd);
     } else {
@@ -516,8 +578,10 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
                                     : surv_entry(surv_tile(i) * kPageTile + lane);
     if (e.x == -INFINITY) return;
     const bool last = e.y < 0.f;
-    gauss_term(e.x, last ? -1.0f - e.y : e.y,
-               last ? last_n : static_cast<float>(P), t, r, f, df);
+    const float sd = last ? -1.0f - e.y : e.y;
+    const float nn = last ? last_n : static_cast<float>(P);
+    if constexpr (RULE) gauss_term_rule(e.x, sd, nn, t, rule, f, df);
+    else gauss_term(e.x, sd, nn, t, r, f, df);
   };
   float tau = tau_lo, prev_step = INFINITY;
   for (int it = 0; it < 64; ++it) {
@@ -674,13 +738,31 @@ hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
                                float alpha, float delta, int32_t *sel,
                                int32_t *count, float *tau_hat, void *ws,
                                hipStream_t stream) {
-  const int r = alpha == 2.0f ? 1 : 2;
+  // r code: 1 and 2 have closed forms; 0 sums the Gauss rules built here
+  const int r = alpha == 2.0f ? 1 : alpha == 1.5f ? 2 : 0;
+  GaussRule rule{};
+  rule.r = 1.0f / (alpha - 1.0f);
+  if (r == 0) {
+    double x[kJacobiNodes], w[kJacobiNodes], hx[kHermiteNodes], hw[kHermiteNodes];
+    if (!gauss_jacobi_rule(static_cast<double>(rule.r), kJacobiNodes, x, w) ||
+        !gauss_hermite_rule(kHermiteNodes, hx, hw))
+      return hipErrorInvalidValue;
+    for (int i = 0; i < kJacobiNodes; ++i) {
+      rule.jx[i] = static_cast<float>(x[i]);
+      rule.jw[i] = static_cast<float>(w[i]);
+    }
+    for (int i = 0; i < kHermiteNodes; ++i) {
+      rule.hx[i] = static_cast<float>(hx[i]);
+      rule.hw[i] = static_cast<float>(hw[i]);
+    }
+  }
   const int units = kv.batch * kv.num_kv_heads;
   auto *masks = static_cast<unsigned long long *>(ws);
-  hipLaunchKernelGGL((k_gauss_tau<G>), dim3(units * G), dim3(kGtThreads), 0,
-                     stream, gstat, kv.seq_lens, kv.batch, kv.num_kv_heads,
-                     kv.page_size, kv.max_pages, alpha - 1.0f, r, delta,
-                     tau_hat, masks);
+  auto gt = r == 0 ? k_gauss_tau<G, true> : k_gauss_tau<G, false>;
+  hipLaunchKernelGGL(gt, dim3(units * G), dim3(kGtThreads), 0, stream, gstat,
+                     kv.seq_lens, kv.batch, kv.num_kv_heads, kv.page_size,
+                     kv.max_pages, alpha - 1.0f, r, delta, tau_hat, masks,
+                     rule);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gauss_collect<G>), dim3(units), dim3(kSelThreads), 0,

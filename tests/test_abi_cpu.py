@@ -10,6 +10,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from sparse_entmax_attention_amd import _binding as B
@@ -101,10 +102,10 @@ def test_validation_errors(lib):
     assert "k must be >= 1" in (_topk(lib, _kv(), k=0) and
                                 lib.ekv_last_error().decode())
     kv = _kv()
-    # alpha must exceed 1; the Gaussian selector is built for 1.5 and 2
+    # alpha must exceed 1; the Gaussian selector is built for 1.1 <= alpha <= 2
     for alpha, want in [(1.0, B.EKV_ERR_INVALID_ARG), (0.5, B.EKV_ERR_INVALID_ARG),
                         (float("nan"), B.EKV_ERR_INVALID_ARG),
-                        (1.25, B.EKV_ERR_UNSUPPORTED)]:
+                        (1.05, B.EKV_ERR_UNSUPPORTED), (2.5, B.EKV_ERR_UNSUPPORTED)]:
         assert lib.ekv_select_gauss(ctypes.byref(kv), FAKE, alpha, 0.5, FAKE,
                                     FAKE, FAKE, None, 0, None) == want
     assert lib.ekv_select_gauss(ctypes.byref(kv), FAKE, 1.5, -1.0, FAKE, FAKE,
@@ -146,3 +147,44 @@ def test_binding_refuses_missing_library(tmp_path):
             B.load_library(str(tmp_path / "missing.so"))
     finally:
         B._lib_handle = saved
+
+
+@pytest.mark.parametrize("beta", [1.0, 4.0 / 3.0, 3.0, 9.0])
+def test_gauss_jacobi_rule_is_exact_to_degree_2n_minus_1(beta):
+    # int_{-1}^{1} (1 + x)^beta (1 + x)^j dx = 2^(beta+j+1) / (beta + j + 1):
+    # every power of (1 + x) up to 2n - 1 is integrated exactly, i.e. every
+    # polynomial of that degree
+    n = 24
+    x, w = B.ekv_quadrature_rule(B.EKV_RULE_JACOBI, beta, n)
+    x, w = np.array(x), np.array(w)
+    assert np.all(np.diff(x) > 0) and x[0] > -1 and x[-1] < 1 and np.all(w > 0)
+    for j in range(2 * n):
+        exact = 2.0 ** (beta + j + 1) / (beta + j + 1)
+        got = float(np.sum(w * (1 + x) ** j))
+        assert abs(got - exact) <= 1e-12 * exact, (j, got, exact)
+
+
+def test_gauss_hermite_rule_moments():
+    # E[X^k] of the standard normal: 0 for odd k, (k-1)!! for even k
+    n = 16
+    x, w = B.ekv_quadrature_rule(B.EKV_RULE_HERMITE, 0.0, n)
+    x, w = np.array(x), np.array(w)
+    assert np.allclose(x, -x[::-1], atol=1e-13) and abs(w.sum() - 1) < 1e-14
+    df = 1.0
+    for k in range(2 * n):
+        got = float(np.sum(w * x ** k))
+        if k % 2:
+            assert abs(got) < 1e-9 * df
+        else:
+            if k:
+                df *= k - 1
+            assert abs(got - df) <= 1e-11 * df, (k, got, df)
+
+
+def test_quadrature_rule_rejects_bad_input():
+    with pytest.raises(B.EkvError):
+        B.ekv_quadrature_rule(B.EKV_RULE_JACOBI, -1.5, 8)
+    with pytest.raises(B.EkvError):
+        B.ekv_quadrature_rule(7, 1.0, 8)
+    with pytest.raises(B.EkvError):
+        B.ekv_quadrature_rule(B.EKV_RULE_HERMITE, 0.0, 65)

@@ -147,7 +147,7 @@ def test_topk_decode(gpu, name, k, alpha):
 
 
 @pytest.mark.parametrize("name", ["cluster_b2_ragged", "cluster_p64", "pool_permuted", "needle32k_gqa"])
-@pytest.mark.parametrize("alpha", [1.5, 2.0])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25, 1.75])
 def test_gauss_decode(gpu, name, alpha):
     inp, host = inputs(name, gpu)
     spec = inp.spec
@@ -406,3 +406,50 @@ def test_selection_with_candidates_beyond_lds(gpu, alpha):
             for tau_, out_ in ((sel_tau, sel_out), (full_tau, full_out)):
                 assert abs(tau_[0, hq] - t) <= TAU_ATOL, (h, j)
                 assert rel_l2(out_[0, hq], o) <= OUT_RTOL_L2, (h, j)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.75, 1.1])
+def test_gauss_threshold_general_alpha_both_rules(gpu, alpha):
+    # Pages of repeated keys have zero variance and pages of keys close to
+    # the query sit far above the threshold: both take the Gauss-Hermite
+    # branch of the expectation; the other pages take the Gauss-Jacobi one.
+    D, P, npg, G = 128, 32, 96, 4
+    print("[case] general-alpha rules, alpha %g" % alpha, flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(23)
+    q = torch.randn(1, G, D, generator=g)
+    k = torch.randn(npg, 1, P, D, generator=g)
+    k[5:9] = k[5:9, :, :1]                       # constant pages: sigma = 0
+    k[40:44] = 0.9 * q[0, 0] + 0.002 * torch.randn(4, 1, P, D, generator=g)
+    k = k.to(torch.bfloat16).to(gpu)
+    v = torch.randn(npg, 1, P, D, generator=g).to(torch.bfloat16).to(gpu)
+    pt = torch.arange(npg, dtype=torch.int32, device=gpu).reshape(1, npg)
+    n = npg * P - 7
+    sl = torch.tensor([n], dtype=torch.int32, device=gpu)
+    kv = ekv.PagedKV(k, v, pt, sl, G)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_gauss(q.to(gpu), alpha, 0.5)
+    torch.cuda.synchronize()
+    keys, vals, qs = f64(k)[:, 0].reshape(-1, D)[:n], f64(v)[:, 0].reshape(-1, D)[:n], f64(q)[0]
+    sc = 1 / math.sqrt(D)
+    _, _, mean, var = O.unit_metadata(keys, P)
+    n_tok = O.page_token_counts(n, P)
+    mu, s2 = zip(*[O.gauss_moments(qs[j], mean, var, sc) for j in range(G)])
+    mu, s2 = np.stack(mu), np.stack(s2)
+    assert (s2[:, 5:9] == 0).all()
+    th = np.array([O.solve_tau_hat(mu[j], s2[j], n_tok, alpha) for j in range(G)])
+    # the Hermite branch is taken: some page mean more than 6 sigma above tau
+    m = (alpha - 1) * mu[0]
+    sd = (alpha - 1) * np.sqrt(s2[0])
+    assert ((m - th[0]) > 6 * sd)[40:44].any()
+    got_th = f64(buf.tau_hat)[0]
+    for j in range(G):
+        assert abs(got_th[j] - th[j]) <= TAU_ATOL, (j, got_th[j], th[j])
+    got = buf.sel[0, 0, :int(buf.count[0, 0])].cpu().numpy()
+    check_gauss_selection(got, mu, s2, n_tok, th, alpha, 0.5)
+    ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
+    tau, out = f64(buf.tau), f64(buf.out)
+    for j in range(G):
+        assert abs(tau[0, j] - ref["tau"][j]) <= TAU_ATOL
+        assert rel_l2(out[0, j], ref["out"][j]) <= OUT_RTOL_L2
