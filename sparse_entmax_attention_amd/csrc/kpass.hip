@@ -114,17 +114,22 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           for (int s2 = 0; s2 < KS; ++s2)
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s2], ring[s][s2], c,
                                                         0, 0, 0);
+          // c[e] of lane n + 16 kb is q-part kb's share of head 4 ps + e on
+          // token n (part 3 is zero).  A butterfly over the four lane groups
+          // leaves every lane with the same sum (c0 + c1) + (c2 + c3), so
+          // lane n + 16 e can write head 4 ps + e's score of token n: one
+          // store with every lane active instead of one per head.
+          float zmine = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p1 = __shfl_down(c[e], 16, kWave);
-            const float p2 = __shfl_down(c[e], 32, kWave);
-            const float z = c[e] + (p1 + p2);
-            const int g = 4 * ps + e;
-            if (g < G)
-              store_if(zr, 4 * (g * cap + j * P + 16 * tt + n), lane < 16 && live,
-                       valid ? z : -INFINITY);
+            const float s1 = c[e] + __shfl_xor(c[e], 16, kWave);
+            const float z = s1 + __shfl_xor(s1, 32, kWave);
             if (valid) pm[ps][e] = fmaxf(pm[ps][e], z);
+            zmine = kb == e ? z : zmine;
           }
+          const int g = 4 * ps + kb;
+          store_if(zr, 4 * (g * cap + j * P + 16 * tt + n), g < G && live,
+                   valid ? zmine : -INFINITY);
         }
         if (tt == NT16 - 1) {
           // the page's maxima, lane g holding head g's
