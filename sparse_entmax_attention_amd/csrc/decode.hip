@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   float pv[U];
 #pragma unroll
   for (int k = 0; k < U4; ++k) {
-    float4 v = make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
-    if (page_k(k, 0) < mps) v = *reinterpret_cast<const float4 *>(pm + page_k(k, 0));
+    // unconditional (clamped into the row, whose length mps is a multiple
+    // of 4), so that all U4 loads are in flight together
+    const float4 v = *reinterpret_cast<const float4 *>(pm + min(page_k(k, 0), mps - 4));
     pv[4 * k] = v.x; pv[4 * k + 1] = v.y; pv[4 * k + 2] = v.z; pv[4 * k + 3] = v.w;
   }
   const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
@@ -749,18 +750,16 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       float pw[RU];
 #pragma unroll
       for (int rr = 0; rr < RU; ++rr) {
+        // unconditional loads (entries past n repeat entry n - 1, with
+        // weight 0), all in flight together
         const int k = base + rr * TPW + sub;
-        pw[rr] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[rr][j] = 0.f;
-        if (k < n) {
-          pw[rr] = seg_p[k];
-          const int pos = seg_pos[k];
-          const int jj = pos >> lgP, t = pos & (P - 1);
-          const int slot =
-              listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
-          load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
-        }
+        const int kc = min(k, n - 1);
+        pw[rr] = k < n ? seg_p[kc] : 0.f;
+        const int pos = seg_pos[kc];
+        const int jj = pos >> lgP, t = pos & (P - 1);
+        const int slot =
+            listed ? dslot[jj] : slots[static_cast<size_t>(u) * max_pages + jj];
+        load8(vpool + pool_row(slot, h, t, H, P, D) + d0, x[rr]);
       }
 #pragma unroll
       for (int rr = 0; rr < RU; ++rr) {
