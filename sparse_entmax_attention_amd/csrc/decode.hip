@@ -384,18 +384,27 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     for (int s0 = wave; s0 < steps; s0 += NW * US) {
       float4 zv[US];
       int zs[US];
+      if (listed) {
+        // The listed pages all hold candidates: their scores and pool slots
+        // (written by the score pass, for the value gather at the end) are
+        // loaded unconditionally, from a clamped index past the list, so
+        // that all of them are in flight together.
 #pragma unroll
-      for (int k = 0; k < US; ++k) {
-        const int jj = (s0 + k * NW) * ppw + sub;
-        zv[k] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        zs[k] = 0;
-        if (jj < n_pg) {
-          const int j = page_of(jj);
-          if (listed || pm[j] > Lf)
-            zv[k] = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(j) * P + t4);
-          // the page's pool slot (written by the score pass), for the
-          // value gather at the end; loaded alongside the scores
-          if (listed && t4 == 0) zs[k] = slots[static_cast<size_t>(u) * max_pages + j];
+        for (int k = 0; k < US; ++k) {
+          const int jj = (s0 + k * NW) * ppw + sub;
+          const int j = dense[min(jj, n_pg - 1)];
+          const float4 v = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(j) * P + t4);
+          zs[k] = slots[static_cast<size_t>(u) * max_pages + j];
+          zv[k] = jj < n_pg ? v : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < US; ++k) {
+          const int jj = (s0 + k * NW) * ppw + sub;
+          zv[k] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          zs[k] = 0;
+          if (jj < n_pg && pm[jj] > Lf)
+            zv[k] = *reinterpret_cast<const float4 *>(zh + static_cast<size_t>(jj) * P + t4);
         }
       }
 #pragma unroll
@@ -560,19 +569,18 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
         unsigned x[KP];
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-          const int e = e0 + k * (NW - 1) * TPW;
-          x[k] = 0u;
-          if (e < n_all) {
-            int w = 0, base = 0;
+          // unconditional (candidates past the last repeat it), so that the
+          // KP loads are in flight together
+          const int e = min(e0 + k * (NW - 1) * TPW, n_all - 1);
+          int w = 0, base = 0;
 #pragma unroll
-            for (int v = 1; v < NW; ++v)
-              if (e >= segs[v]) { w = v; base = segs[v]; }
-            const int pos = cpos[w * CSEG + (e - base)];
-            const int slot = dslot[pos >> lgP];
-            const char *row = reinterpret_cast<const char *>(
-                vpool + pool_row(slot, h, pos & (P - 1), H, P, D));
-            x[k] = *reinterpret_cast<const unsigned *>(row + 128 * li);
-          }
+          for (int v = 1; v < NW; ++v)
+            if (e >= segs[v]) { w = v; base = segs[v]; }
+          const int pos = cpos[w * CSEG + (e - base)];
+          const int slot = dslot[pos >> lgP];
+          const char *row = reinterpret_cast<const char *>(
+              vpool + pool_row(slot, h, pos & (P - 1), H, P, D));
+          x[k] = *reinterpret_cast<const unsigned *>(row + 128 * li);
         }
 #pragma unroll
         for (int k = 0; k < KP; ++k) asm volatile("" ::"v"(x[k]));
