@@ -27,6 +27,13 @@ CASES = {
     "cluster_b2_ragged": ("cluster_128k_b4", {"batch": 2, "seq_len": 9000}, 102),
     "cluster_p64": ("cluster_1m", {"seq_len": 65536 + 3}, 103),
     "pool_permuted": ("ragged_pool_b16", {"batch": 3, "len_range": (700, 6000)}, 104),
+    # group sizes 8 and 2 (two query-head passes of the key pass's MFMA, and
+    # lanes of absent heads dropped), bf16 at head_dim 64, pages of 16
+    "gqa8_d128": ("cluster_128k_b4", {"batch": 2, "seq_len": 7000, "group": 8,
+                                       "num_kv_heads": 2}, 105),
+    "gqa2_d64_p16": ("needle_32k_gqa", {"seq_len": 5000, "group": 2, "head_dim": 64,
+                                         "page_size": 16, "num_kv_heads": 3,
+                                         "needles": 9}, 106),
 }
 
 _cache = {}
@@ -117,7 +124,8 @@ def test_page_scores(gpu, name):
 
 @pytest.mark.parametrize("name,k", [("needle4k_f32_d64", 32), ("needle32k_gqa", 32),
                                     ("needle32k_gqa", 3), ("cluster_p64", 16),
-                                    ("cluster_p64", 200)])
+                                    ("cluster_p64", 200), ("gqa8_d128", 40),
+                                    ("gqa2_d64_p16", 64)])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_topk_decode(gpu, name, k, alpha):
     inp, host = inputs(name, gpu)
@@ -146,7 +154,8 @@ def test_topk_decode(gpu, name, k, alpha):
     print("near-cutoff swaps:", swaps)
 
 
-@pytest.mark.parametrize("name", ["cluster_b2_ragged", "cluster_p64", "pool_permuted", "needle32k_gqa"])
+@pytest.mark.parametrize("name", ["cluster_b2_ragged", "cluster_p64", "pool_permuted", "needle32k_gqa",
+                                  "gqa8_d128", "gqa2_d64_p16"])
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25, 1.75])
 def test_gauss_decode(gpu, name, alpha):
     inp, host = inputs(name, gpu)
