@@ -241,22 +241,8 @@ __device__ __forceinline__ void rebuild_page_meta(const typename E::T *kpool, in
   const __amdgpu_buffer_rsrc_t rows = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T *>(kpool + pool_row(slot, h, 0, H, P, D)),
       static_cast<short>(0), n * D * static_cast<int>(sizeof(T)), 0x00020000);
-  // One coordinate at a time, its n tokens in registers (the second read of
-  // the rows comes from the cache).
-#pragma unroll 1
-  for (int c = 0; c < CPL; ++c) {
-    const int voff = (lane * CPL + c) * static_cast<int>(sizeof(T));
-    float x[64];
-#pragma unroll
-    for (int t = 0; t < 64; ++t) {
-      const int soff = t * D * static_cast<int>(sizeof(T));
-      if constexpr (sizeof(T) == 2)
-        x[t] = __uint_as_float(static_cast<uint32_t>(
-                                   __builtin_amdgcn_raw_buffer_load_b16(rows, voff, soff, 0))
-                               << 16);
-      else
-        x[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows, voff, soff, 0));
-    }
+  // Statistics of coordinate lane * CPL + c from its n values xv(t).
+  auto stats = [&](auto xv, int c) {
     float mn = INFINITY, mx = -INFINITY, s = 0.f;
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
@@ -265,9 +251,10 @@ __device__ __forceinline__ void rebuild_page_meta(const typename E::T *kpool, in
       for (int i = 0; i < MAXT; ++i) {
         const int t = tg + i * TG;
         if (t < 64 && t < n) {
-          mn = fminf(mn, x[t]);
-          mx = fmaxf(mx, x[t]);
-          part += x[t];
+          const float x = xv(t);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+          part += x;
         }
       }
       s = tg == 0 ? part : s + part;
@@ -281,7 +268,7 @@ __device__ __forceinline__ void rebuild_page_meta(const typename E::T *kpool, in
       for (int i = 0; i < MAXT; ++i) {
         const int t = tg + i * TG;
         if (t < 64 && t < n) {
-          const float dv = x[t] - mean;
+          const float dv = xv(t) - mean;
           part = fmaf(dv, dv, part);
         }
       }
@@ -295,6 +282,43 @@ __device__ __forceinline__ void rebuild_page_meta(const typename E::T *kpool, in
     if (gauss) {
       gauss[meta_row(slot, h, 0, H, D) + d] = mean;
       gauss[meta_row(slot, h, 1, H, D) + d] = v / static_cast<float>(n);
+    }
+  };
+  if constexpr (sizeof(T) == 2 && CPL == 2) {
+    // A lane's two bfloat16 coordinates are adjacent: one 4-byte load per
+    // token brings both (the lower address in the low half), so the page is
+    // read once, with all 64 loads in flight together.
+    uint32_t w[64];
+#pragma unroll
+    for (int t = 0; t < 64; ++t)
+      w[t] = __builtin_amdgcn_raw_buffer_load_b32(rows, lane * 4, t * D * 2, 0);
+    // (the values are unpacked at each use rather than kept unpacked: the
+    // empty asm stops the compiler from holding 64 more registers)
+    auto half = [&](int t, uint32_t mask, int sh) {
+      uint32_t x = w[t];
+      asm volatile("" : "+v"(x));
+      return __uint_as_float((x << sh) & mask);
+    };
+    stats([&](int t) { return half(t, 0xffff0000u, 16); }, 0);
+    stats([&](int t) { return half(t, 0xffff0000u, 0); }, 1);
+  } else {
+    // One coordinate at a time, its n tokens in registers (the second read
+    // of the rows comes from the cache).
+#pragma unroll 1
+    for (int c = 0; c < CPL; ++c) {
+      const int voff = (lane * CPL + c) * static_cast<int>(sizeof(T));
+      float x[64];
+#pragma unroll
+      for (int t = 0; t < 64; ++t) {
+        const int soff = t * D * static_cast<int>(sizeof(T));
+        if constexpr (sizeof(T) == 2)
+          x[t] = __uint_as_float(static_cast<uint32_t>(
+                                     __builtin_amdgcn_raw_buffer_load_b16(rows, voff, soff, 0))
+                                 << 16);
+        else
+          x[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows, voff, soff, 0));
+      }
+      stats([&](int t) { return x[t]; }, c);
     }
   }
 }
