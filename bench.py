@@ -444,10 +444,10 @@ def main():
             speedups["topk_over_%s" % base] = round(
                 results[base]["median_ms"] / results["topk"]["median_ms"], 3)
 
-    cpu = None
+    cpu, cpu_more = None, None
     n_cpu = B * H if args.cpu_units < 0 else args.cpu_units
     if n_cpu > 0:
-        cpu = cpu_baseline(inp, spec, min(n_cpu, B * H), alpha, delta, log)
+        cpu, cpu_more = cpu_baseline(inp, spec, min(n_cpu, B * H), alpha, delta, log)
 
     line = {
         "metric": "decode tokens/s at 1M ctx (1 GPU); achieved HBM GB/s vs peak",
@@ -471,6 +471,7 @@ def main():
         "hbm_frac_of_peak": round(head["hbm_gbps"] / PEAK_HBM_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_more": cpu_more,
         "speedups": speedups,
         "meta_build_ms": round(meta_build_ms, 4),
         "hbm_read_probe_gbps": round(read_probe_gbps, 1),
@@ -506,18 +507,49 @@ def cpu_baseline(inp, spec, n_units, alpha, delta, log):
         t0 = time.perf_counter()
         O.decode_unit(qs, keys, vals, P, scale, alpha, "gauss", delta=delta)
         times.append(time.perf_counter() - t0)
+        if u == 0:
+            qs0, keys0, vals0 = qs, keys, vals
+    units_per_step = spec.batch * spec.num_kv_heads
+
+    def rate(per_unit_s):
+        return round(spec.batch / (per_unit_s * units_per_step), 6)
+
+    # The same oracle on unit 0 for the full-cache baselines (every token,
+    # every query head of the group), still on one thread.
+    more = {}
+    for kind, fn in (("entmax_full", lambda q: O.entmax_attend(q, keys0, vals0, scale, alpha)),
+                     ("softmax_full", lambda q: O.softmax_attend(q, keys0, vals0, scale))):
+        log("[bench] oracle %s, unit 0" % kind)
+        t0 = time.perf_counter()
+        for g in range(G):
+            fn(qs0[g])
+        dt = time.perf_counter() - t0
+        more[kind] = {"value": rate(dt), "unit": "tokens/s", "cores": 1,
+                      "sample": "every token of unit 0 for its %d query heads, "
+                                "fp64 numpy, %.2f s; step time = that x %d units"
+                                % (G, dt, units_per_step)}
     if limiter is not None:
         limiter.restore_original_limits()
+    # Unit 0 of the Gaussian step again with numpy free to use every core
+    # of this process (the oracle is not parallelised beyond that).
+    cores = len(os.sched_getaffinity(0))
+    log("[bench] oracle unit 0 on %d cores" % cores)
+    t0 = time.perf_counter()
+    O.decode_unit(qs0, keys0, vals0, P, scale, alpha, "gauss", delta=delta)
+    dt = time.perf_counter() - t0
+    more["gauss_all_cores"] = {"value": rate(dt), "unit": "tokens/s",
+                               "cores": cores,
+                               "sample": "unit 0 of the Gaussian step, numpy "
+                                         "free to use every core, %.2f s; step "
+                                         "time = that x %d units" % (dt, units_per_step)}
     per_unit = statistics.mean(times)
-    units_per_step = spec.batch * spec.num_kv_heads
-    step_s = per_unit * units_per_step
-    return {"value": round(spec.batch / step_s, 6), "unit": "tokens/s",
+    return {"value": rate(per_unit), "unit": "tokens/s",
             "cores": 1, "kind": "oracle",
             "sample": "%d of %d (sequence, KV head) units of one decode step "
                       "(metadata build, Gaussian scoring, threshold estimate, "
                       "selection, entmax over the kept pages), fp64 numpy, "
                       "%.2f s per unit; step time = per-unit time x %d units"
-                      % (n_units, units_per_step, per_unit, units_per_step)}
+                      % (n_units, units_per_step, per_unit, units_per_step)}, more
 
 
 if __name__ == "__main__":
