@@ -147,8 +147,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU decode step only; this build "
-              "runs on one GPU (got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+        print("bench.py measures the decode step on one GPU only; units are "
+              "independent, and the multi-GPU split is not implemented "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 
