@@ -217,6 +217,41 @@ def test_full_cache_entmax(gpu, name, alpha):
             assert np.abs(pg - p).max() < 1e-4
 
 
+@pytest.mark.parametrize("name", ["needle4k_f32_d64", "pool_permuted", "gqa2_d64_p16"])
+@pytest.mark.parametrize("alpha", [1.1, 1.75, 3.0])
+def test_decode_other_alpha(gpu, name, alpha):
+    # The exact-threshold shortcuts cover alpha in {1.5, 2}; elsewhere the
+    # threshold is bisected and p = max(z - tau, 0)^r uses the general power
+    # (r = 10 at alpha 1.1, a concave square root at alpha 3).  Checked over
+    # a top-k selection and over the full cache.
+    inp, host = inputs(name, gpu)
+    spec = inp.spec
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_topk(inp.q, alpha, 24)
+    torch.cuda.synchronize()
+    sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
+    tau, out = f64(buf.tau), f64(buf.out)
+    buf.entmax(inp.q, alpha, selected=False)
+    torch.cuda.synchronize()
+    f_tau, f_out = f64(buf.tau), f64(buf.out)
+    P, G, sc = spec.page_size, spec.group, scale_of(spec)
+    for b, h in _units(inp):
+        qs, keys, vals = host.unit(b, h)
+        ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given",
+                            pages=sel[b, h, :cnt[b, h]])
+        for j in range(G):
+            hq = h * G + j
+            assert abs(tau[b, hq] - ref["tau"][j]) <= TAU_ATOL, (b, h, j)
+            assert rel_l2(out[b, hq], ref["out"][j]) <= OUT_RTOL_L2, (b, h, j)
+            z = (alpha - 1) * O.token_scores(qs[j], keys, sc)
+            t = O.entmax_threshold(z, alpha)
+            p = O.entmax_probs(z, t, alpha)
+            assert abs(f_tau[b, hq] - t) <= TAU_ATOL, (b, h, j)
+            assert rel_l2(f_out[b, hq], (p[:, None] * vals).sum(0)) <= OUT_RTOL_L2
+
+
 @pytest.mark.parametrize("name", ["needle4k_f32_d64", "needle32k_gqa", "cluster_b2_ragged", "pool_permuted"])
 def test_full_cache_softmax(gpu, name):
     inp, host = inputs(name, gpu)
