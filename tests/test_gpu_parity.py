@@ -452,6 +452,58 @@ def test_selection_with_candidates_beyond_lds(gpu, alpha):
                 assert rel_l2(out_[0, hq], o) <= OUT_RTOL_L2, (h, j)
 
 
+@pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (1.25, 0.0)])
+def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta):
+    # Keys without structure give every page a score spread of about 1, so
+    # no 64-page tile can be pruned: all 157 tiles survive and are keep
+    # candidates, more than the selector holds on chip (128 of each), and
+    # the rest are read from memory in the Newton passes and the keep test.
+    D, P, npg, G = 64, 16, 10000, 2
+    n = npg * P - 5
+    print("[case] Gaussian selector beyond LDS tiles, alpha %g" % alpha, flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(41)
+    k = torch.randn(npg, 1, P, D, generator=g).to(gpu)
+    v = torch.randn(npg, 1, P, D, generator=g).to(gpu)
+    pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
+    sl = torch.tensor([n], dtype=torch.int32, device=gpu)
+    q = torch.randn(1, G, D, generator=g).to(gpu)
+    kv = ekv.PagedKV(k, v, pt, sl, G)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_gauss(q, alpha, delta)
+    torch.cuda.synchronize()
+    sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
+    tau_hat, tau, out = f64(buf.tau_hat), f64(buf.tau), f64(buf.out)
+    rows = pt.cpu().numpy()[0]
+    keys = f64(k)[rows, 0].reshape(-1, D)[:n]
+    vals = f64(v)[rows, 0].reshape(-1, D)[:n]
+    qs = f64(q)[0]
+    sc = 1 / math.sqrt(D)
+    _, _, mean, var = O.unit_metadata(keys, P)
+    n_tok = O.page_token_counts(n, P)
+    mu, s2 = zip(*[O.gauss_moments(qs[j], mean, var, sc) for j in range(G)])
+    mu, s2 = np.stack(mu), np.stack(s2)
+    th = np.array([O.solve_tau_hat(mu[j], s2[j], n_tok, alpha) for j in range(G)])
+    # every tile survives the pruning (page maxima estimate m + 8.5 s above
+    # the lower bound on the threshold)
+    m, sd = (alpha - 1) * mu, (alpha - 1) * np.sqrt(s2)
+    lo = (m.max(axis=1) - P ** (-(alpha - 1)))[:, None]
+    alive = m + 8.5 * sd > lo
+    n_tl = (npg + 63) // 64
+    assert n_tl > 128
+    assert all(alive[:, 64 * t:64 * (t + 1)].any(axis=1).all() for t in range(n_tl))
+    for j in range(G):
+        assert abs(tau_hat[0, j] - th[j]) <= TAU_ATOL, j
+    got = sel[0, 0, :cnt[0, 0]]
+    assert cnt[0, 0] >= 1 and (np.diff(got) > 0).all()
+    check_gauss_selection(got, mu, s2, n_tok, th, alpha, delta)
+    ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
+    for j in range(G):
+        assert abs(tau[0, j] - ref["tau"][j]) <= TAU_ATOL, j
+        assert rel_l2(out[0, j], ref["out"][j]) <= OUT_RTOL_L2, j
+
+
 @pytest.mark.parametrize("alpha", [1.25, 1.75, 1.1])
 def test_gauss_threshold_general_alpha_both_rules(gpu, alpha):
     # Pages of repeated keys have zero variance and pages of keys close to
