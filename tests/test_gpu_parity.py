@@ -452,6 +452,52 @@ def test_selection_with_candidates_beyond_lds(gpu, alpha):
                 assert rel_l2(out_[0, hq], o) <= OUT_RTOL_L2, (h, j)
 
 
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_threshold_with_pages_beyond_lds(gpu, alpha):
+    # 20,000 pages whose scores all lie within a few thousandths: more page
+    # maxima than the threshold step holds in registers (16,384, the rest
+    # are read again), more pages above its bracket than it lists on chip
+    # (4,096) and more candidate scores than it stages (8,192).  Checked
+    # over the full cache and over a selection of every page.
+    D, P, npg, G = 64, 16, 20000, 2
+    n = npg * P - 7
+    print("[case] threshold with pages beyond LDS, alpha %g" % alpha, flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(43)
+    k = (3e-4 * torch.randn(npg, 1, P, D, generator=g)).to(gpu)
+    v = torch.randn(npg, 1, P, D, generator=g).to(gpu)
+    pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
+    sl = torch.tensor([n], dtype=torch.int32, device=gpu)
+    q = torch.randn(1, G, D, generator=g).to(gpu)
+    kv = ekv.PagedKV(k, v, pt, sl, G)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.step_topk(q, alpha, npg)
+    torch.cuda.synchronize()
+    assert (buf.count == npg).all()
+    sel_tau, sel_out = f64(buf.tau), f64(buf.out)
+    buf.entmax(q, alpha, selected=False)
+    torch.cuda.synchronize()
+    full_tau, full_out = f64(buf.tau), f64(buf.out)
+    rows = pt.cpu().numpy()[0]
+    keys = f64(k)[rows, 0].reshape(-1, D)[:n]
+    vals = f64(v)[rows, 0].reshape(-1, D)[:n]
+    qh = f64(q)[0]
+    sc = 1 / math.sqrt(D)
+    for j in range(G):
+        z = (alpha - 1) * O.token_scores(qh[j], keys, sc)
+        t = O.entmax_threshold(z, alpha)
+        # the bracket's lower end is a lower bound on tau, so every page
+        # maximum and every score above tau lies above it
+        pm = np.array([z[i:i + P].max() for i in range(0, n, P)])
+        assert (pm > t).sum() > 4096 and (z > t).sum() > 8192
+        p = O.entmax_probs(z, t, alpha)
+        o = (p[:, None] * vals).sum(0)
+        for tau_, out_ in ((sel_tau, sel_out), (full_tau, full_out)):
+            assert abs(tau_[0, j] - t) <= TAU_ATOL, j
+            assert rel_l2(out_[0, j], o) <= OUT_RTOL_L2, j
+
+
 @pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (1.25, 0.0)])
 def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta):
     # Keys without structure give every page a score spread of about 1, so
