@@ -36,10 +36,17 @@ Pinning (see tests/test_oracle_*.py):
     J_r = (r-1) J_(r-2) - c J_(r-1), Monte Carlo).
   * solve_tau_hat: pinned (zero-variance limit equals the exact entmax
     threshold of the repeated means; monotonicity; uniqueness).
-  * gauss_keep: parity unpinned beyond self-consistency.  The estimated
-    page maximum mu + sigma*sqrt(2 ln n) and the comparison in z units are
-    readings of the summary's Gaussian selector paragraph; no page fixes
-    them numerically.  Limits (Delta -> inf keeps every page) are pinned.
+  * page_max_estimate: pinned by the defining property of the classical
+    bound it reads the 'estimated maximum score' as (at least the Monte
+    Carlo expected maximum of n draws, exact at n = 1, within 35 % above the
+    mean at n = 16 and 64).
+  * gauss_keep: parity unpinned beyond self-consistency.  The comparison
+    (alpha - 1) * estimate > tau_hat - delta in z units is a reading of the
+    summary's Gaussian selector paragraph; no page fixes it numerically.
+    Limits (Delta -> inf keeps every page) are pinned.
+  Planted mistakes in these functions (tests/oracle_mutants.py: dropped
+  factors, wrong signs, roots, exponents, indices and tie rules) each fail
+  at least one pin (tests/test_oracle_mutants.py).
   * softmax_attend: pinned (shift invariance, alpha -> 1 limit of entmax).
   * dropped_mass, softmax_dropped_mass, support_recall,
     matched_budget_quality: pinned (covering sets give zero dropped mass,

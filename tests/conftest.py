@@ -23,3 +23,12 @@ def gpu():
     import sparse_entmax_attention_amd as ekv
     ekv.load_library()  # raises when libentmaxkv.so has not been built
     return torch.device("cuda:0")
+
+
+def pytest_sessionstart(session):
+    # A planted oracle mistake, for the mutant check (test_oracle_mutants.py
+    # runs the pin tests in a child process with this variable set).
+    name = os.environ.get("EKV_ORACLE_MUTANT")
+    if name:
+        import oracle_mutants
+        oracle_mutants.apply(name)

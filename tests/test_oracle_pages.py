@@ -268,6 +268,22 @@ def test_tau_hat_is_the_unique_root(alpha):
         assert th >= m.max() - 1.0
 
 
+def test_page_max_estimate_bounds_the_expected_maximum():
+    # mu + sigma sqrt(2 ln n) is the classical upper bound on the expected
+    # largest of n draws of N(mu, sigma^2); it is exact at n = 1 and, measured
+    # above mu, within 35 % of the expected maximum at n = 16 and 64 (the
+    # bound tightens as n grows).  Checked against Monte Carlo maxima.
+    rng = np.random.default_rng(17)
+    mu, s2 = np.array([0.3]), np.array([2.25])
+    assert O.page_max_estimate(mu, s2, np.array([1]))[0] == pytest.approx(0.3)
+    for n in (2, 16, 64):
+        est = O.page_max_estimate(mu, s2, np.array([n]))[0]
+        mc = (0.3 + 1.5 * rng.standard_normal((200000, n))).max(axis=1).mean()
+        assert est >= mc
+        if n >= 16:
+            assert (est - 0.3) <= 1.35 * (mc - 0.3)
+
+
 def test_gauss_keep_limits():
     rng = np.random.default_rng(13)
     G, n = 4, 60
