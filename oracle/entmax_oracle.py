@@ -44,6 +44,9 @@ Pinning (see tests/test_oracle_*.py):
     (alpha - 1) * estimate > tau_hat - delta in z units is a reading of the
     summary's Gaussian selector paragraph; no page fixes it numerically.
     Limits (Delta -> inf keeps every page) are pinned.
+  * bf16_bits_to_f64, unit_tokens: pinned (exact decoding of known bit
+    patterns; a scatter of numbered tokens through a random page table
+    gathers back in order).
   Planted mistakes in these functions (tests/oracle_mutants.py: dropped
   factors, wrong signs, roots, exponents, indices and tie rules) each fail
   at least one pin (tests/test_oracle_mutants.py).

@@ -126,6 +126,73 @@ def _bisect_half_exponent(z, alpha, tol=1e-13):
     return _get("entmax_threshold_bisect")(z, 1.0 + 1.0 / (alpha - 1.0), tol)
 
 
+def _bf16_wrong_shift(bits):
+    w = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15)
+    return w.view(np.float32).astype(np.float64)
+
+
+def _unit_tokens_offset_order(pool, page_table_row, kv_head, n_tokens):
+    # rows of each page taken in reverse
+    P = pool.shape[2]
+    rows = _get("unit_tokens")(pool, page_table_row, kv_head, n_tokens)
+    out = rows.copy()
+    for p0 in range(0, n_tokens, P):
+        p1 = min(p0 + P, n_tokens)
+        out[p0:p1] = rows[p0:p1][::-1]
+    return out
+
+
+def _softmax_lse_unshifted(q, keys, vals, scale):
+    o, lse = _get("softmax_attend")(q, keys, vals, scale)
+    s = _get("token_scores")(q, keys, scale)
+    return o, lse - float(np.max(s))
+
+
+def _entmax_attend_unnormalised_tau(q, keys, vals, scale, alpha):
+    # threshold taken on the scores instead of z = (alpha - 1) s
+    s = _get("token_scores")(q, keys, scale)
+    tau = M.entmax_threshold(s, alpha)
+    p = M.entmax_probs(s, tau, alpha)
+    return p @ vals, tau, p
+
+
+def _dropped_mass_of_kept(q, keys, kept_tokens, scale, alpha):
+    d, p, tau = _get("dropped_mass")(q, keys, kept_tokens, scale, alpha)
+    return 1.0 - d, p, tau
+
+
+def _softmax_dropped_unnormalised(q, keys, kept_tokens, scale):
+    s = M.token_scores(q, keys, scale)
+    w = np.exp(s - np.max(s))
+    mask = np.ones(len(s), dtype=bool)
+    mask[np.asarray(kept_tokens, dtype=np.int64)] = False
+    return float(w[mask].sum())
+
+
+def _recall_over_kept(p_full, kept_tokens):
+    support = np.flatnonzero(np.asarray(p_full) > 0.0)
+    kept = np.zeros(len(p_full), dtype=bool)
+    kept[np.asarray(kept_tokens, dtype=np.int64)] = True
+    return float(kept[support].sum()) / max(int(kept.sum()), 1)
+
+
+def _keep_fallback_smallest_gap(mu, sigma2, n_tok, tau_hat, alpha, delta):
+    kept = _get("gauss_keep")(mu, sigma2, n_tok, tau_hat, alpha, delta)
+    if len(kept) != 1:
+        return kept
+    G, n = mu.shape
+    zhat = np.stack([(alpha - 1.0) * M.page_max_estimate(mu[h], sigma2[h], n_tok)
+                     for h in range(G)])
+    if any(zhat[h, kept[0]] > tau_hat[h] - delta for h in range(G)):
+        return kept
+    gap = np.max(zhat - np.asarray(tau_hat)[:, None], axis=0)
+    return np.array([int(np.argmin(gap))], dtype=np.int64)
+
+
+def _keep_first_head_only(mu, sigma2, n_tok, tau_hat, alpha, delta):
+    return _get("gauss_keep")(mu[:1], sigma2[:1], n_tok, tau_hat[:1], alpha, delta)
+
+
 MUTANTS = {
     "entmax15_wrong_root": ("entmax_threshold", _entmax15_wrong_root),
     "sparsemax_extra_element": ("entmax_threshold", _sparsemax_extra_element),
@@ -144,6 +211,15 @@ MUTANTS = {
     "counts_full_last": ("page_token_counts", _counts_full_last),
     "excess_standard_order_off": ("excess_standard", _excess_standard_order_off),
     "bisect_reciprocal_exponent": ("entmax_threshold_bisect", _bisect_half_exponent),
+    "bf16_wrong_shift": ("bf16_bits_to_f64", _bf16_wrong_shift),
+    "unit_tokens_rows_reversed": ("unit_tokens", _unit_tokens_offset_order),
+    "softmax_lse_unshifted": ("softmax_attend", _softmax_lse_unshifted),
+    "entmax_attend_on_scores": ("entmax_attend", _entmax_attend_unnormalised_tau),
+    "dropped_mass_of_kept": ("dropped_mass", _dropped_mass_of_kept),
+    "softmax_dropped_unnormalised": ("softmax_dropped_mass", _softmax_dropped_unnormalised),
+    "recall_over_kept": ("support_recall", _recall_over_kept),
+    "keep_fallback_smallest_gap": ("gauss_keep", _keep_fallback_smallest_gap),
+    "keep_first_head_only": ("gauss_keep", _keep_first_head_only),
 }
 
 

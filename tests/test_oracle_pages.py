@@ -315,6 +315,23 @@ def test_gauss_selector_recovers_support_on_single_token_pages():
     assert np.array_equal(res["out"], full["out"])
 
 
+def test_unit_tokens_round_trip():
+    # Logical token i of a sequence lives at offset i % P of the physical
+    # slot the page table names for page i // P.  Scattering numbered tokens
+    # into a pool by that rule, with a random page table, two KV heads and a
+    # short last page, the gather must give them back in order.
+    rng = np.random.default_rng(23)
+    P, D, H, n = 4, 3, 2, 13
+    n_pages = (n + P - 1) // P
+    table = rng.permutation(7)[:n_pages]
+    pool = rng.standard_normal((7, H, P, D))
+    seq = np.arange(n * D, dtype=np.float64).reshape(n, D)
+    for i in range(n):
+        pool[table[i // P], 1, i % P] = seq[i]
+    np.testing.assert_array_equal(O.unit_tokens(pool, table, 1, n), seq)
+    assert not np.array_equal(O.unit_tokens(pool, table, 0, n), seq)
+
+
 def test_bf16_decoding():
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x7F7F], dtype=np.uint16)
     vals = O.bf16_bits_to_f64(bits)
