@@ -30,6 +30,9 @@ Pinning (see tests/test_oracle_*.py):
   * gauss_moments: pinned (exact variance of the score of a page's tokens
     in the single-coordinate case; Monte Carlo).
   * select_topk: pinned (brute force over subsets, nesting, k >= n).
+  * group_bound: pinned (on one-token pages the group value is the largest
+    exact token score over the query heads; on any page it bounds every
+    head's token scores and is attained by one head's bound).
   * gauss_excess_moment, excess_standard: pinned (numerical quadrature of
     the defining integral for r in {1, 2, 4/3, 3, 4, 7.5} on both sides of
     the series switch, the closed forms at r = 1 and 2, the recurrence
@@ -67,7 +70,7 @@ from scipy import special as _sp
 __all__ = [
     "bf16_bits_to_f64", "unit_tokens", "page_token_counts", "page_metadata",
     "unit_metadata", "token_scores", "bbox_bound", "gauss_moments",
-    "select_topk", "excess_standard", "gauss_excess_moment",
+    "group_bound", "select_topk", "excess_standard", "gauss_excess_moment",
     "gauss_normaliser", "solve_tau_hat",
     "page_max_estimate", "gauss_keep", "entmax_threshold",
     "entmax_threshold_bisect", "entmax_probs", "entmax_attend",
@@ -202,6 +205,18 @@ def gauss_moments(q: np.ndarray, mean: np.ndarray, var: np.ndarray,
 # ---------------------------------------------------------------------------
 # Top-k page selection  [Technical Summary, §2.B.1]
 # ---------------------------------------------------------------------------
+
+def group_bound(ub: np.ndarray) -> np.ndarray:
+    """Ranking value of every page for a KV head's G query heads.
+
+    ub: [G][n_pages], each row one query head's box bound.  Reading: one
+    selection serves all query heads of a KV head, so a page is ranked by a
+    value that bounds the score of any of its tokens for any of those heads;
+    the tightest such value built from the per-head bounds is their largest,
+    g_p = max_h ub[h, p].
+    """
+    return np.asarray(ub, dtype=np.float64).max(axis=0)
+
 
 def select_topk(g: np.ndarray, k: int) -> np.ndarray:
     """The min(k, n) pages with the largest bound g, returned ascending.
@@ -505,7 +520,7 @@ def decode_unit(qs: np.ndarray, keys: np.ndarray, vals: np.ndarray, P: int,
         kmin, kmax, mean, var = unit_metadata(keys, P)
     if selector == "topk":
         ub = np.stack([bbox_bound(qs[h], kmin, kmax, scale) for h in range(G)])
-        g = ub.max(axis=0)
+        g = group_bound(ub)
         sel = select_topk(g, k)
         res.update(ub=ub, g=g)
     elif selector == "gauss":

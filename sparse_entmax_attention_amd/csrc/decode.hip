@@ -331,9 +331,12 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   float Lf = static_cast<float>(L);
   if (static_cast<double>(Lf) > L) Lf = nextafterf(Lf, -INFINITY);
 
-  // Pages whose maximum exceeds L: each wave lists those of its 64-page
-  // tiles (in page order within the wave), then the lists are laid end to
-  // end in `dense`.
+  // Pages whose maximum exceeds L: each wave lists those it holds, then the
+  // lists are laid end to end in `dense`.  The order is fixed but not
+  // ascending: lane l of wave w holds pages 4 (64 w + l) + e + 4 k
+  // kTauThreads, and the wave lists them slice k by slice k and, within a
+  // slice, e by e (pages 256 w + 4 l, then 256 w + 4 l + 1, ...).  Nothing
+  // that reads `dense` or `dslot` relies on their order.
   int npw = 0;
   const unsigned long long below = (1ull << lane) - 1ull;
   auto list_page = [&](int j, float v) {  // called by whole waves

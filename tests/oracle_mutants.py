@@ -193,6 +193,14 @@ def _keep_first_head_only(mu, sigma2, n_tok, tau_hat, alpha, delta):
     return _get("gauss_keep")(mu[:1], sigma2[:1], n_tok, tau_hat[:1], alpha, delta)
 
 
+def _group_bound_head0(ub):
+    return np.asarray(ub, dtype=np.float64)[0].copy()
+
+
+def _group_bound_mean(ub):
+    return np.asarray(ub, dtype=np.float64).mean(axis=0)
+
+
 MUTANTS = {
     "entmax15_wrong_root": ("entmax_threshold", _entmax15_wrong_root),
     "sparsemax_extra_element": ("entmax_threshold", _sparsemax_extra_element),
@@ -220,6 +228,8 @@ MUTANTS = {
     "recall_over_kept": ("support_recall", _recall_over_kept),
     "keep_fallback_smallest_gap": ("gauss_keep", _keep_fallback_smallest_gap),
     "keep_first_head_only": ("gauss_keep", _keep_first_head_only),
+    "group_bound_head0": ("group_bound", _group_bound_head0),
+    "group_bound_mean": ("group_bound", _group_bound_mean),
 }
 
 

@@ -70,10 +70,10 @@ def test_needle_32k_gqa_topk_all_units(gpu):
         for b in range(spec.batch):
             for h in range(spec.num_kv_heads):
                 qs, keys, vals = unit_copy(inp, b, h)
-                kmin, kmax, _, _ = O.unit_metadata(keys, P)
-                g = np.max([O.bbox_bound(qs[j], kmin, kmax, sc) for j in range(G)], axis=0)
+                want = O.decode_unit(qs, keys, vals, P, sc, alpha, "topk",
+                                     k=spec.topk)
                 got = buf.sel[b, h, :int(buf.count[b, h].item())].cpu().numpy()
-                check_topk_selection(got, g, spec.topk)
+                check_topk_selection(got, want, spec.topk)
                 ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
                 for j in range(G):
                     hq = h * G + j
@@ -118,10 +118,9 @@ def test_cluster_1m_all_legs_sampled(gpu):
     for b, h in [(0, 1), (0, 6)]:
         print("[unit] topk h=%d" % h, flush=True)
         qs, keys, vals = unit_copy(inp, b, h)
-        kmin, kmax, _, _ = O.unit_metadata(keys, P)
-        g = np.max([O.bbox_bound(qs[j], kmin, kmax, sc) for j in range(G)], axis=0)
+        want = O.decode_unit(qs, keys, vals, P, sc, alpha, "topk", k=spec.topk)
         got = buf.sel[b, h, :int(buf.count[b, h].item())].cpu().numpy()
-        check_topk_selection(got, g, spec.topk)
+        check_topk_selection(got, want, spec.topk)
         ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
         for j in range(G):
             assert abs(tau[b, h * G + j] - ref["tau"][j]) <= TAU_ATOL

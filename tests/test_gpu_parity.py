@@ -141,11 +141,10 @@ def test_topk_decode(gpu, name, k, alpha):
     swaps = 0
     for b, h in _units(inp):
         qs, keys, vals = host.unit(b, h)
-        kmin, kmax, _, _ = O.unit_metadata(keys, P)
-        g = np.max([O.bbox_bound(qs[j], kmin, kmax, sc) for j in range(G)], axis=0)
+        want = O.decode_unit(qs, keys, vals, P, sc, alpha, "topk", k=k)
         got = sel[b, h, :cnt[b, h]]
         assert (np.diff(got) > 0).all()
-        swaps += check_topk_selection(got, g, k)
+        swaps += check_topk_selection(got, want, k)
         ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
         for j in range(G):
             hq = h * G + j
@@ -393,13 +392,13 @@ def test_topk_ties_across_tiles(gpu):
     buf.step_topk(q, 1.5, k)
     torch.cuda.synchronize()
     # the last page is short: its box can differ, so rank it with the oracle
-    keys = f64(kk[:, 0]).reshape(-1, D)[:npg * P - 7]
-    kmin, kmax, _, _ = O.unit_metadata(keys, P)
     qs = f64(q)[0]
     for h in range(2):
-        gmax = np.max([O.bbox_bound(qs[h * 2 + j], kmin, kmax, 1 / math.sqrt(D))
-                       for j in range(2)], axis=0)
-        want = list(O.select_topk(gmax, k))
+        keys = f64(kk[:, h]).reshape(-1, D)[:npg * P - 7]
+        vals = f64(vv[:, h]).reshape(-1, D)[:npg * P - 7]
+        ref = O.decode_unit(qs[h * 2:h * 2 + 2], keys, vals, P, 1 / math.sqrt(D),
+                            1.5, "topk", k=k)
+        want = list(ref["sel"])
         assert int(buf.count[0, h]) == k
         assert list(buf.sel[0, h, :k].cpu().numpy()) == want
 

@@ -101,9 +101,9 @@ def test_random_shape_step(gpu, seed):
                     assert abs(tau_hat[b, h * G + j] - th[j]) <= TAU_ATOL, (b, h, j)
                 check_gauss_selection(got, mu, s2, n_tok, th, alpha, c["delta"])
             else:
-                g = np.max([O.bbox_bound(qs[j], kmin, kmax, sc)
-                            for j in range(G)], axis=0)
-                check_topk_selection(got, g, c["k"])
+                want = O.decode_unit(qs, keys, vals, P, sc, alpha, "topk",
+                                     k=c["k"])
+                check_topk_selection(got, want, c["k"])
             ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
             toks = ref["tokens"]
             for j in range(G):

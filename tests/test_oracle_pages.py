@@ -130,6 +130,49 @@ def test_topk_nesting_and_all():
     assert list(O.select_topk(g, 80)) == list(range(50))
 
 
+def test_group_bound_on_one_token_pages_is_the_best_head_score():
+    """With one token per page each head's box is a point, so the group's
+    ranking value must be the largest exact score over the query heads and
+    top-k must keep the pages of the k largest of those."""
+    rng = np.random.default_rng(81)
+    G, D, N, k = 4, 8, 40, 6
+    scale = 1.0 / math.sqrt(D)
+    for _ in range(5):
+        qs = rng.normal(size=(G, D)) * rng.uniform(0.2, 3.0, size=(G, 1))
+        keys = rng.normal(size=(N, D))
+        vals = rng.normal(size=(N, D))
+        res = O.decode_unit(qs, keys, vals, 1, scale, 1.5, "topk", k=k)
+        best = np.array([max(scale * sum(qs[h, d] * keys[i, d] for d in range(D))
+                             for h in range(G)) for i in range(N)])
+        np.testing.assert_allclose(res["g"], best, rtol=1e-12, atol=1e-12)
+        order = sorted(range(N), key=lambda i: (-best[i], i))
+        assert list(res["sel"]) == sorted(order[:k])
+
+
+def test_group_bound_bounds_every_head_and_is_attained():
+    """On pages of many tokens the group value bounds the score of every
+    token of the page for every query head of the group, and it is one of
+    the heads' own box bounds (the tightest value with that property)."""
+    rng = np.random.default_rng(82)
+    G, D, P, N = 4, 16, 16, 16 * 12 + 5
+    scale = 1.0 / math.sqrt(D)
+    qs = rng.normal(size=(G, D)) * np.array([[0.3], [1.0], [2.0], [0.7]])
+    keys = rng.normal(size=(N, D))
+    # needles aligned to the last head only, in pages 3 and 8
+    for i in (3 * P + 2, 8 * P + 11):
+        keys[i] = 3.0 * qs[G - 1] / np.linalg.norm(qs[G - 1])
+    res = O.decode_unit(qs, keys, rng.normal(size=(N, D)), P, scale, 1.5,
+                        "topk", k=4)
+    g, ub = res["g"], res["ub"]
+    for p in range(len(g)):
+        toks = range(p * P, min((p + 1) * P, N))
+        top = max(scale * float(np.dot(qs[h], keys[i])) for h in range(G) for i in toks)
+        assert g[p] >= top - 1e-12
+        assert any(g[p] == ub[h, p] for h in range(G))
+        assert all(g[p] >= ub[h, p] for h in range(G))
+    assert {3, 8} <= set(res["sel"].tolist())
+
+
 # --- Gaussian expectation and threshold estimate ---------------------------------
 
 @pytest.mark.parametrize("r", [1, 2])
