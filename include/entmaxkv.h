@@ -16,7 +16,8 @@
  *    two structs below are HOST structs, read during the call only.
  *  - The caller allocates and owns every buffer.  The library never
  *    allocates or frees device memory, never synchronises and never copies
- *    device to host.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    device to host.  (ekv_entmax_decode_noalloc alone works in a static
+ *    device array of the library instead of a caller's workspace.)  Work is enqueued on `stream` (a hipStream_t passed as
  *    void*; NULL is the default stream).  Results are valid once the caller
  *    has synchronised with that stream.
  *  - Unit: one (sequence b, KV head h) pair.  Query heads of KV head h are
@@ -35,8 +36,9 @@
  *    below ceil(seq_lens[b]/P) with 1 <= count <= that page count.
  *  - Determinism: identical inputs give bit-identical outputs (no floating
  *    point atomics; every reduction has a fixed order).
- *  - Concurrency: no global mutable state besides the per-thread error text;
- *    calls on different streams with disjoint outputs and workspaces may run
+ *  - Concurrency: no global mutable state besides the per-thread error text
+ *    and the per-device scratch of ekv_entmax_decode_noalloc; calls on
+ *    different streams with disjoint outputs and workspaces may run
  *    concurrently.
  */
 #ifndef ENTMAXKV_H
@@ -239,6 +241,27 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
                              const int32_t *count, float *out, float *tau,
                              float *probs, void *ws, size_t ws_bytes,
                              void *stream);
+
+/*
+ * ekv_entmax_decode_noalloc - ekv_entmax_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a static device array of EKV_NOALLOC_SCRATCH_BYTES in the
+ * library, one per GPU, held until the process ends; the call allocates
+ * nothing (its first call on a GPU looks up that GPU's copy of the array).
+ * Arguments, results and errors as for ekv_entmax_decode; a cache whose
+ * workspace, ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0), exceeds
+ * EKV_NOALLOC_SCRATCH_BYTES returns EKV_ERR_WORKSPACE and launches nothing.
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (different streams, or threads) race and must be serialised by the
+ * caller.  No part of the array needs clearing between calls.
+ */
+#define EKV_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB */
+ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
+                                     float scale, float alpha,
+                                     const int32_t *sel, const int32_t *count,
+                                     float *out, float *tau, float *probs,
+                                     void *stream);
 
 /*
  * The three steps of ekv_entmax_decode, for callers that time or interleave

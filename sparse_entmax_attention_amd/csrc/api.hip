@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -145,6 +146,46 @@ hipError_t with_g(const ekv_paged_kv &kv, F &&f) {
   } while (0)
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// Workspace of ekv_entmax_decode_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` is only
+// a host-side stand-in for the symbol; its device address on a GPU comes
+// from hipGetSymbolAddress with that GPU current, taken once per device and
+// kept in g_scratch.
+constexpr size_t kScratchBytes = static_cast<size_t>(EKV_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the GPU that runs `stream`.
+ekv_status scratch_on(hipStream_t stream, void **ptr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "finding the stream's device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(EKV_ERR_UNSUPPORTED, "device %d: the scratch is kept for devices 0..%d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess)
+      return hip_status(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return hip_status(e, "hipSetDevice");
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(EKV_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return EKV_OK;
+}
 
 }  // namespace
 
@@ -343,6 +384,24 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
   EKV_TRY(ekv_entmax_scores(kv, q, scale, alpha, sel, count, ws, ws_bytes, stream));
   EKV_TRY(ekv_entmax_threshold(kv, alpha, sel, count, tau, out, ws, ws_bytes, stream));
   return ekv_entmax_apply(kv, alpha, sel, count, out, probs, ws, ws_bytes, stream);
+}
+
+ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
+                                     float scale, float alpha,
+                                     const int32_t *sel, const int32_t *count,
+                                     float *out, float *tau, float *probs,
+                                     void *stream) {
+  EKV_TRY(check_kv(kv, true, true));
+  const size_t need = ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0);
+  if (need > kScratchBytes)
+    return fail(EKV_ERR_WORKSPACE,
+                "this cache needs %zu bytes of decode workspace; the static "
+                "scratch holds %zu (use ekv_entmax_decode with a workspace)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  EKV_TRY(scratch_on(as_stream(stream), &ws));
+  return ekv_entmax_decode(kv, q, scale, alpha, sel, count, out, tau, probs,
+                           ws, kScratchBytes, stream);
 }
 
 ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,
