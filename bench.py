@@ -226,8 +226,10 @@ def main():
             # the tail page's metadata refresh runs inside the scoring launch
             ("score_gauss", lambda: buf.refresh_score(q, ekv.EKV_SCORE_GAUSS)),
             ("select_gauss", lambda: buf.select_gauss(alpha, delta)),
+            # the selector's threshold estimates are the decode's hint
             ("entmax_scores", lambda: ekv.ekv_entmax_scores(
-                kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
+                kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode,
+                tau_hint=buf.tau_hat)),
             ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
                 kv, alpha, buf.sel, buf.count, buf.tau, buf.out, buf.ws_decode)),
             ("entmax_apply", lambda: ekv.ekv_entmax_apply(

@@ -228,6 +228,18 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
  *   sel, count   as produced by the selectors; sel == NULL means every page
  *                of every sequence (the full-cache entmax baseline), and
  *                count is then ignored.
+ *   tau_hint     [batch][H_q] float32 or NULL: an estimate of each head's
+ *                threshold, typically tau_hat from ekv_select_gauss.  The
+ *                result does not depend on it (up to the floating-point
+ *                order of the support sums); it only lets the key pass keep
+ *                the scores above hint - 1/32 instead of all of them.  The
+ *                threshold step checks that the kept scores alone reach the
+ *                normalisation at that floor, which proves every support
+ *                score was kept; when they do not (a hint too high, or more
+ *                than 8192 kept scores or 2048 pages with kept scores per
+ *                head) it recomputes that head's scores from the keys and
+ *                solves as without a hint, which is slower.  Used for
+ *                bfloat16 keys only, and ignored when probs is not NULL.
  *   out          [batch][H_q][head_dim] float32.
  *   tau          [batch][H_q] float32 or NULL.
  *   probs        [batch][H_q][max_pages*P] float32 or NULL (debug): p of
@@ -238,9 +250,9 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
  */
 ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,
-                             const int32_t *count, float *out, float *tau,
-                             float *probs, void *ws, size_t ws_bytes,
-                             void *stream);
+                             const int32_t *count, const float *tau_hint,
+                             float *out, float *tau, float *probs, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /*
  * ekv_entmax_decode_noalloc - ekv_entmax_decode without a workspace
@@ -260,15 +272,17 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
 ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
                                      float scale, float alpha,
                                      const int32_t *sel, const int32_t *count,
-                                     float *out, float *tau, float *probs,
-                                     void *stream);
+                                     const float *tau_hint, float *out,
+                                     float *tau, float *probs, void *stream);
 
 /*
  * The three steps of ekv_entmax_decode, for callers that time or interleave
  * them.  They must be called in this order with the same kv, sel, count,
  * alpha and workspace.
  *   ekv_entmax_scores     gathers the selected keys and writes z to the
- *                         workspace with per-chunk maxima.
+ *                         workspace with per-page maxima (with tau_hint,
+ *                         only the scores above hint - 1/32, see
+ *                         ekv_entmax_decode).
  *   ekv_entmax_threshold  solves tau per query head (tau may be NULL: it is
  *                         then kept in the workspace only) and gathers the
  *                         values of the support: with a selection (sel not
@@ -283,8 +297,8 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
  */
 ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,
-                             const int32_t *count, void *ws, size_t ws_bytes,
-                             void *stream);
+                             const int32_t *count, const float *tau_hint,
+                             void *ws, size_t ws_bytes, void *stream);
 ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
                                 const int32_t *sel, const int32_t *count,
                                 float *tau, float *out, void *ws,

@@ -70,12 +70,13 @@ _SIGNATURES = {
                                   _c_p]),
     "ekv_entmax_decode": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
                                    _c_f32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
-                                   _c_size, _c_p]),
+                                   _c_p, _c_size, _c_p]),
     "ekv_entmax_decode_noalloc": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p,
                                            _c_f32, _c_f32, _c_p, _c_p, _c_p,
-                                           _c_p, _c_p, _c_p]),
+                                           _c_p, _c_p, _c_p, _c_p]),
     "ekv_entmax_scores": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
-                                   _c_f32, _c_p, _c_p, _c_p, _c_size, _c_p]),
+                                   _c_f32, _c_p, _c_p, _c_p, _c_p, _c_size,
+                                   _c_p]),
     "ekv_entmax_threshold": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_f32,
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_size,
                                       _c_p]),
@@ -252,31 +253,33 @@ def ekv_select_gauss(kv: PagedKV, gstat, alpha: float, delta: float, sel,
 
 
 def ekv_entmax_decode(kv: PagedKV, q, scale: float, alpha: float, sel, count,
-                      out, tau=None, probs=None, ws=None, stream=None) -> None:
+                      out, tau=None, probs=None, ws=None, stream=None,
+                      tau_hint=None) -> None:
     s = kv.struct()
     _check(load_library().ekv_entmax_decode(
         ctypes.byref(s), _ptr(q), float(scale), float(alpha), _ptr(sel),
-        _ptr(count), _ptr(out), _ptr(tau), _ptr(probs), _ptr(ws),
-        ws.numel() if ws is not None else 0, _stream(stream)),
+        _ptr(count), _ptr(tau_hint), _ptr(out), _ptr(tau), _ptr(probs),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
         "ekv_entmax_decode")
 
 
 def ekv_entmax_decode_noalloc(kv: PagedKV, q, scale: float, alpha: float, sel,
                               count, out, tau=None, probs=None,
-                              stream=None) -> None:
+                              stream=None, tau_hint=None) -> None:
     s = kv.struct()
     _check(load_library().ekv_entmax_decode_noalloc(
         ctypes.byref(s), _ptr(q), float(scale), float(alpha), _ptr(sel),
-        _ptr(count), _ptr(out), _ptr(tau), _ptr(probs), _stream(stream)),
+        _ptr(count), _ptr(tau_hint), _ptr(out), _ptr(tau), _ptr(probs),
+        _stream(stream)),
         "ekv_entmax_decode_noalloc")
 
 
 def ekv_entmax_scores(kv: PagedKV, q, scale: float, alpha: float, sel, count,
-                      ws, stream=None) -> None:
+                      ws, stream=None, tau_hint=None) -> None:
     s = kv.struct()
     _check(load_library().ekv_entmax_scores(
         ctypes.byref(s), _ptr(q), float(scale), float(alpha), _ptr(sel),
-        _ptr(count), _ptr(ws), ws.numel(), _stream(stream)),
+        _ptr(count), _ptr(tau_hint), _ptr(ws), ws.numel(), _stream(stream)),
         "ekv_entmax_scores")
 
 

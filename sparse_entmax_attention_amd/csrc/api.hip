@@ -323,8 +323,8 @@ ekv_status ekv_select_gauss(const ekv_paged_kv *kv, const float *gstat,
 
 ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,
-                             const int32_t *count, void *ws, size_t ws_bytes,
-                             void *stream) {
+                             const int32_t *count, const float *tau_hint,
+                             void *ws, size_t ws_bytes, void *stream) {
   EKV_TRY(check_kv(kv, true, false));
   EKV_TRY(check_scale(scale));
   EKV_TRY(check_alpha(alpha));
@@ -335,7 +335,7 @@ ekv_status ekv_entmax_scores(const ekv_paged_kv *kv, const float *q,
   const hipError_t e = with_edg(*kv, [&](auto E, auto D, auto G) {
     return ekv::launch_entmax_scores<decltype(E), decltype(D)::value,
                                      decltype(G)::value>(
-        *kv, q, scale, alpha, sel, count, ws, as_stream(stream));
+        *kv, q, scale, alpha, sel, count, tau_hint, ws, as_stream(stream));
   });
   return hip_status(e, "ekv_entmax_scores launch");
 }
@@ -344,7 +344,7 @@ ekv_status ekv_entmax_threshold(const ekv_paged_kv *kv, float alpha,
                                 const int32_t *sel, const int32_t *count,
                                 float *tau, float *out, void *ws,
                                 size_t ws_bytes, void *stream) {
-  EKV_TRY(check_kv(kv, false, true));
+  EKV_TRY(check_kv(kv, true, true));
   EKV_TRY(check_alpha(alpha));
   EKV_TRY(check_sel(sel, count));
   if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
@@ -376,12 +376,14 @@ ekv_status ekv_entmax_apply(const ekv_paged_kv *kv, float alpha,
 
 ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
                              float scale, float alpha, const int32_t *sel,
-                             const int32_t *count, float *out, float *tau,
-                             float *probs, void *ws, size_t ws_bytes,
-                             void *stream) {
+                             const int32_t *count, const float *tau_hint,
+                             float *out, float *tau, float *probs, void *ws,
+                             size_t ws_bytes, void *stream) {
   EKV_TRY(check_kv(kv, true, true));
   if (!out) return fail(EKV_ERR_INVALID_ARG, "out is required");
-  EKV_TRY(ekv_entmax_scores(kv, q, scale, alpha, sel, count, ws, ws_bytes, stream));
+  // the debug probabilities need every score: the hint is not used then
+  EKV_TRY(ekv_entmax_scores(kv, q, scale, alpha, sel, count,
+                            probs ? nullptr : tau_hint, ws, ws_bytes, stream));
   EKV_TRY(ekv_entmax_threshold(kv, alpha, sel, count, tau, out, ws, ws_bytes, stream));
   return ekv_entmax_apply(kv, alpha, sel, count, out, probs, ws, ws_bytes, stream);
 }
@@ -389,8 +391,8 @@ ekv_status ekv_entmax_decode(const ekv_paged_kv *kv, const float *q,
 ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
                                      float scale, float alpha,
                                      const int32_t *sel, const int32_t *count,
-                                     float *out, float *tau, float *probs,
-                                     void *stream) {
+                                     const float *tau_hint, float *out,
+                                     float *tau, float *probs, void *stream) {
   EKV_TRY(check_kv(kv, true, true));
   const size_t need = ekv_workspace_size(EKV_OP_ENTMAX_DECODE, kv, 0);
   if (need > kScratchBytes)
@@ -400,8 +402,8 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
                 need, kScratchBytes);
   void *ws = nullptr;
   EKV_TRY(scratch_on(as_stream(stream), &ws));
-  return ekv_entmax_decode(kv, q, scale, alpha, sel, count, out, tau, probs,
-                           ws, kScratchBytes, stream);
+  return ekv_entmax_decode(kv, q, scale, alpha, sel, count, tau_hint, out, tau,
+                           probs, ws, kScratchBytes, stream);
 }
 
 ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,

@@ -37,7 +37,10 @@ DecodeWs decode_ws_layout(const ekv_paged_kv &kv) {
   w.ctr = al(w.part_s + units * mc * G * 4);  // chunks finished, per unit
   w.done = al(w.ctr + (units + 1) * 4);  // + heads left to the apply step
   w.slot = al(w.done + units * G * 4);  // pool slot per selected page
-  w.total = al(w.slot + units * static_cast<size_t>(kv.max_pages) * 4);
+  w.floor = al(w.slot + units * static_cast<size_t>(kv.max_pages) * 4);  // per head
+  w.qz = al(w.floor + units * G * 4);  // (alpha-1) scale q per head
+  w.mask = al(w.qz + units * G * D * 4);  // candidate bits per page and head
+  w.total = al(w.mask + units * G * static_cast<size_t>(pm_stride(kv.max_pages)) * 8);
   return w;
 }
 
@@ -194,17 +197,66 @@ __device__ __forceinline__ double block_incl_scan_d(double x, double *smem) {
   return base + x;
 }
 
+// Scores of every selected token of one query head, recomputed on the vector
+// units from the keys (z = <qz, k>, qz = (alpha-1) scale q) and written in
+// the plain layout with -inf past each page's valid tokens, together with
+// the page maxima: what an unhinted key pass leaves for that head.  Used
+// when a hinted key pass kept too few scores.  Whole block; ends with a
+// barrier after which the block sees the new values.
+template <class E, int D>
+__device__ void recompute_head_scores(const typename E::T *kpool,
+                                      const int32_t *page_table,
+                                      const int32_t *seq_lens,
+                                      const int32_t *sel, const int32_t *slots,
+                                      const float *qz, int u, int cnt, int H,
+                                      int P, int max_pages, float *zh,
+                                      float *pm) {
+  constexpr int LPT = D / 8, TPW = kWave / LPT;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int sub = lane / LPT, li = lane % LPT, d0 = li * 8;
+  const int nwv = blockDim.x / kWave;
+  const int b = u / H, h = u % H;
+  float qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qv[j] = qz[d0 + j];
+  for (int j = wave; j < cnt; j += nwv) {
+    const int lp = sel ? sel[static_cast<size_t>(u) * max_pages + j] : j;
+    const int nt = page_tokens(lp, seq_lens[b], P);
+    const int slot = slots[static_cast<size_t>(u) * max_pages + j];
+    float mx = -FLT_MAX;
+    for (int t0 = 0; t0 < P; t0 += TPW) {
+      const int t = t0 + sub;
+      float x[8];
+      load8(kpool + pool_row(slot, h, t, H, P, D) + d0, x);
+      float a = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a = fmaf(qv[k], x[k], a);
+      a = group_sum<LPT>(a);
+      const bool valid = t < nt;
+      if (li == 0) zh[static_cast<size_t>(j) * P + t] = valid ? a : -INFINITY;
+      if (valid) mx = fmaxf(mx, a);
+    }
+    mx = group_max<kWave>(mx);
+    if (lane == 0) pm[j] = mx;
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
-    const float *__restrict__ zbuf, const float *__restrict__ pmax,
+    float *__restrict__ zbuf, float *__restrict__ pmax,
     const typename E::T *__restrict__ vpool,
+    const typename E::T *__restrict__ kpool,
     const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, int H, int G, int P, int max_pages,
     int cap, int r, float rg, float *__restrict__ tau_ws,
     float *__restrict__ tau_user, float *__restrict__ out,
     int32_t *__restrict__ done, int32_t *__restrict__ ctr,
-    const int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
+    const int32_t *__restrict__ slots, int32_t *__restrict__ undone,
+    const float *__restrict__ floor_ws, const float *__restrict__ qz,
+    const unsigned long long *__restrict__ pmask) {
   constexpr int NW = kTauThreads / kWave;
   constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
   constexpr int CSEG = kTauCandCap / NW;  // staged candidates per wave
@@ -235,9 +287,180 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   const int lgP = __builtin_ctz(P);  // page sizes are powers of two
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int mps = pm_stride(max_pages);
-  const float *zh = zbuf + static_cast<size_t>(ug) * cap;
-  const float *pm = pmax + static_cast<size_t>(ug) * mps;
+  float *zh = zbuf + static_cast<size_t>(ug) * cap;
+  float *pm = pmax + static_cast<size_t>(ug) * mps;
   constexpr int U = 32, U4 = U / 4;
+  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
+  const unsigned long long below = (1ull << lane) - 1ull;
+
+  // Results of the front end: the largest score M, a lower bound L on tau
+  // (Lf: the largest float not above L) and, in LDS, every score above L
+  // (per-wave segments of cand / cpos, counts in s_ccnt).  With `listed`,
+  // cpos holds (index into dense) * P + t, else (selection index) * P + t.
+  float M = -FLT_MAX, Lf = -FLT_MAX;
+  double Md = 0.0, L = 0.0;
+  bool listed = false;
+  int n_pg = cnt;
+
+  // Hinted key pass: only scores above the floor f were kept, packed per
+  // page with a bit mask.  They are staged here; if they alone give
+  // sum (z - f)_+^r >= 1, then tau >= f (the full sum is larger), every
+  // score of the support is among them and f serves as L.  Otherwise the
+  // head's scores are recomputed in full and the plain front end runs.
+  const float fl = floor_ws[ug];
+  bool hinted = fl > -INFINITY;
+  if (hinted) {
+    constexpr int MCAP = (NW * SEGP * static_cast<int>(sizeof(int))) /
+                         static_cast<int>(sizeof(unsigned long long));
+    unsigned long long *dmask = reinterpret_cast<unsigned long long *>(&cpages[0][0]);
+    const unsigned long long *mk = pmask + static_cast<size_t>(ug) * mps;
+    // 1. pages holding candidates, in page order, with their masks and pool
+    // slots (the slots loaded beside the masks, all in flight together)
+    const int32_t *uslots = slots + static_cast<size_t>(u) * max_pages;
+    int n_cp = 0;
+    for (int base = 0; base < cnt; base += kTauThreads * 4) {
+      unsigned long long m4[4];
+      int s4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = min(base + k * kTauThreads + tid, cnt - 1);
+        m4[k] = mk[j];
+        s4[k] = uslots[j];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = base + k * kTauThreads + tid;
+        const bool has = j < cnt && m4[k] != 0ull;
+        int tot;
+        const int rk = tile_rank<kTauThreads>(has, red_i, tot);
+        if (has && n_cp + rk < MCAP) {
+          dense[n_cp + rk] = j;
+          dmask[n_cp + rk] = m4[k];
+          dslot[n_cp + rk] = s4[k];
+        }
+        n_cp += tot;
+      }
+    }
+    lds_barrier();
+    // 2. stage them in page order, candidate e of the head going to segment
+    // e / per_seg (per_seg = ceil(C / NW)): the per-page counts are scanned
+    // (each thread owns 4 consecutive listed pages, offsets kept in dslot),
+    // then every thread takes candidates tid, tid + kTauThreads, ..., finds
+    // its page by bisection over the offsets and its token as the rank-th
+    // set bit of the page's mask; all of a thread's loads are in flight
+    // together.
+    int *coff = reinterpret_cast<int *>(hist);  // kTauBins >= MCAP entries
+    int C = 0;
+    if (n_cp <= MCAP) {
+      int cnt4[4], loc = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int li = 4 * tid + k;
+        cnt4[k] = li < n_cp ? __popcll(dmask[li]) : 0;
+        loc += cnt4[k];
+      }
+      int pre = block_excl_scan<kTauThreads>(loc, red_i, C);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int li = 4 * tid + k;
+        if (li < n_cp) coff[li] = pre;
+        pre += cnt4[k];
+      }
+    }
+    lds_barrier();
+    int nc = 0;
+    float mloc = -FLT_MAX;
+    const int per_seg = (C + NW - 1) / NW;
+    if (n_cp <= MCAP && per_seg <= CSEG) {
+      constexpr int EU = 4;  // candidates per thread per round
+      for (int e0 = 0; e0 < C; e0 += EU * kTauThreads) {
+        float zv[EU];
+        int posv[EU];
+#pragma unroll
+        for (int k = 0; k < EU; ++k) {
+          const int e = min(e0 + k * kTauThreads + tid, C - 1);
+          int lo = 0, hi = n_cp - 1;  // last listed page with coff <= e
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (coff[mid] <= e) lo = mid; else hi = mid - 1;
+          }
+          int rk = e - coff[lo];
+          unsigned long long m = dmask[lo];
+          int t = 0;  // position of the rk-th set bit of m
+#pragma unroll
+          for (int w = 32; w >= 1; w >>= 1) {
+            const unsigned long long lowm = m & ((1ull << w) - 1ull);
+            const int c = __popcll(lowm);
+            if (rk >= c) {
+              rk -= c;
+              m >>= w;
+              t += w;
+            } else {
+              m = lowm;
+            }
+          }
+          // position: listed page index * P + token (slots in dslot)
+          zv[k] = zh[static_cast<size_t>(dense[lo]) * P + (e - coff[lo])];
+          posv[k] = lo * P + t;
+        }
+#pragma unroll
+        for (int k = 0; k < EU; ++k) {
+          const int e = e0 + k * kTauThreads + tid;
+          if (e < C) {
+            const int w = e / per_seg, i = e - w * per_seg;
+            cand[w * CSEG + i] = zv[k];
+            cpos[w * CSEG + i] = posv[k];
+            mloc = fmaxf(mloc, zv[k]);
+          }
+        }
+      }
+      nc = max(0, min(per_seg, C - wave * per_seg));
+    }
+    if (lane == 0) s_ccnt[wave] = (n_cp <= MCAP && per_seg <= CSEG) ? nc : CSEG + 1;
+    lds_barrier();
+    bool fits = n_cp <= MCAP;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) fits &= s_ccnt[w] <= CSEG;
+    // 3. M and the check sum (z - f)_+^r >= 1 (double), over the staged
+    // candidates.
+    double fs = 0.0;
+    if (fits) {
+      const int ncw = s_ccnt[wave];
+      for (int i = lane; i < ncw; i += kWave) {
+        const double y = static_cast<double>(cand[wave * CSEG + i]) - fl;
+        fs += (r == 1) ? y : (r == 2) ? y * y : pow(y, static_cast<double>(rg));
+      }
+    }
+    fs = wave_sum_d(fs);
+    mloc = wave_max_f(mloc);
+    if (lane == 0) {
+      red_d[wave] = fs;
+      s_wmax[wave] = mloc;
+    }
+    lds_barrier();
+    double fsum = 0.0;
+    float mall = -FLT_MAX;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      fsum += red_d[w];
+      mall = fmaxf(mall, s_wmax[w]);
+    }
+    if (fits && fsum >= 1.0) {
+      M = mall;
+      Md = M;
+      L = fl;
+      Lf = fl;
+      listed = true;
+      n_pg = n_cp;
+    } else {
+      recompute_head_scores<E, D>(kpool, page_table, seq_lens, sel, slots,
+                                  qz + static_cast<size_t>(ug) * D, u, cnt, H,
+                                  P, max_pages, zh, pm);
+      hinted = false;
+    }
+  }
+
+  if (!hinted) {
 
   // Page maxima, read once with 16-byte loads, issued before the page count
   // is known (rows are padded to a multiple of 4; entries past the count
@@ -245,6 +468,8 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   // (e < 4, k < U/4); pages beyond U * kTauThreads (very long selections)
   // are re-read when needed.
   static_assert(kTauMaxBins <= kTauBins, "page-maximum bins reuse hist");
+  static_assert(kTauBins * sizeof(unsigned int) >= 2048 * sizeof(int),
+                "hinted candidate offsets reuse hist");
   constexpr int CACHED = kTauThreads * U;
   auto page_k = [&](int k, int e) { return 4 * tid + e + 4 * k * kTauThreads; };
   float pv[U];
@@ -255,7 +480,6 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     const float4 v = *reinterpret_cast<const float4 *>(pm + min(page_k(k, 0), mps - 4));
     pv[4 * k] = v.x; pv[4 * k + 1] = v.y; pv[4 * k + 2] = v.z; pv[4 * k + 3] = v.w;
   }
-  const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
   // Slices k (4 kTauThreads pages each) that hold selected pages: the others
   // are skipped (the test is uniform, and no load depends on it).
   const int nsl = min(U4, (cnt + 4 * kTauThreads - 1) / (4 * kTauThreads));
@@ -277,10 +501,10 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   mloc = wave_max_f(mloc);
   if (lane == 0) s_wmax[wave] = mloc;
   lds_barrier();
-  float M = s_wmax[0];
+  M = s_wmax[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) M = fmaxf(M, s_wmax[w]);
-  const double Md = M;
+  Md = M;
 
   // Tighter lower bracket from the page maxima within 1 of M: with C_b the
   // number of page maxima in bins >= b (all at least the bin's lower edge
@@ -322,13 +546,13 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   Lloc = wave_max_d(Lloc);
   if (lane == 0) s_wL[wave] = Lloc;
   lds_barrier();
-  double L = s_wL[0];
+  L = s_wL[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) L = fmax(L, s_wL[w]);
   // Snap down to a multiple of 2^-24 so that z - L is exact in double.
   L = floor(L * 16777216.0) / 16777216.0;
   // For a float z, z > L exactly when z > Lf, the largest float <= L.
-  float Lf = static_cast<float>(L);
+  Lf = static_cast<float>(L);
   if (static_cast<double>(Lf) > L) Lf = nextafterf(Lf, -INFINITY);
 
   // Pages whose maximum exceeds L: each wave lists those it holds, then the
@@ -338,7 +562,6 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   // slice, e by e (pages 256 w + 4 l, then 256 w + 4 l + 1, ...).  Nothing
   // that reads `dense` or `dslot` relies on their order.
   int npw = 0;
-  const unsigned long long below = (1ull << lane) - 1ull;
   auto list_page = [&](int j, float v) {  // called by whole waves
     const bool flag = j < cnt && v > Lf;
     const unsigned long long ball = __ballot(flag);
@@ -358,7 +581,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   if (lane == 0) s_npg[wave] = npw;
   if (tid == 0) s_nlist = 0;
   lds_barrier();
-  bool listed = true;
+  listed = true;
   int n_listed = 0, seg0 = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -370,8 +593,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   if (listed)
     for (int i = lane; i < npw; i += kWave) dense[seg0 + i] = cpages[wave][i];
   lds_barrier();
-  const int n_pg = listed ? n_listed : cnt;
-  auto page_of = [&](int jj) { return listed ? dense[jj] : jj; };
+  n_pg = listed ? n_listed : cnt;
 
   // Stage the candidates z > L in LDS, wave w appending to its own segment
   // cand[w * CSEG ..] in a fixed order (no atomics, so the order does not
@@ -431,6 +653,8 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     if (lane == 0) s_ccnt[wave] = nc;
   }
   lds_barrier();
+  }  // plain front end
+  auto page_of = [&](int jj) { return listed ? dense[jj] : jj; };
   bool staged = true;
 #pragma unroll
   for (int w = 0; w < NW; ++w) staged &= s_ccnt[w] <= CSEG;
@@ -473,7 +697,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
       // segment order) goes to lane e % 64, slot e / 64.
       // Segment starts in scalar registers (wave-uniform), so that locating
       // a candidate is a compare chain rather than dependent LDS reads.
-      constexpr int R = 16;
+      constexpr int R = 32;
       int segs[NW + 1];
       segs[0] = 0;
 #pragma unroll
@@ -580,7 +804,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
           for (int v = 1; v < NW; ++v)
             if (e >= segs[v]) { w = v; base = segs[v]; }
           const int pos = cpos[w * CSEG + (e - base)];
-          const int slot = dslot[pos >> lgP];
+          const int slot = dslot[pos >> lgP];  // listed positions (also hinted)
           const char *row = reinterpret_cast<const char *>(
               vpool + pool_row(slot, h, pos & (P - 1), H, P, D));
           x[k] = *reinterpret_cast<const unsigned *>(row + 128 * li);
@@ -1653,16 +1877,20 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
   const int r = exponent_code(alpha, rg);
   hipLaunchKernelGGL((k_entmax_tau<E, D>), dim3(kv.batch * kv.num_kv_heads * G),
                      dim3(kTauThreads), 0, stream,
-                     reinterpret_cast<const float *>(w + L.z),
-                     reinterpret_cast<const float *>(w + L.cmax),
-                     static_cast<const typename E::T *>(kv.v), kv.page_table,
+                     reinterpret_cast<float *>(w + L.z),
+                     reinterpret_cast<float *>(w + L.cmax),
+                     static_cast<const typename E::T *>(kv.v),
+                     static_cast<const typename E::T *>(kv.k), kv.page_table,
                      kv.seq_lens, sel, count, kv.num_kv_heads, G, kv.page_size,
                      kv.max_pages, kv.max_pages * kv.page_size, r, rg,
                      reinterpret_cast<float *>(w + L.tau), tau, out,
                      reinterpret_cast<int32_t *>(w + L.done),
                      reinterpret_cast<int32_t *>(w + L.ctr),
                      reinterpret_cast<const int32_t *>(w + L.slot),
-                     reinterpret_cast<int32_t *>(w + L.ctr) + kv.batch * kv.num_kv_heads);
+                     reinterpret_cast<int32_t *>(w + L.ctr) + kv.batch * kv.num_kv_heads,
+                     reinterpret_cast<const float *>(w + L.floor),
+                     reinterpret_cast<const float *>(w + L.qz),
+                     reinterpret_cast<const unsigned long long *>(w + L.mask));
   return hipGetLastError();
 }
 

@@ -43,8 +43,14 @@ __host__ __device__ inline int pm_stride(int max_pages) {
 }
 
 struct DecodeWs {
-  size_t z, cmax, tau, part_o, part_s, ctr, done, slot, total;
+  size_t z, cmax, tau, part_o, part_s, ctr, done, slot, floor, qz, mask, total;
 };
+
+// Scores below (tau hint - kHintMargin) are not kept by a hinted key pass.
+// The margin is in z units; the Gaussian selector's estimate lies within
+// about 0.01 of the exact threshold on the clustered workloads, and a hint
+// that proves too high is caught and repaired by the threshold step.
+constexpr float kHintMargin = 0.03125f;
 DecodeWs decode_ws_layout(const ekv_paged_kv &kv);
 struct SoftmaxWs {
   size_t part_m, part_l, part_o, total;
@@ -71,8 +77,8 @@ hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
 template <class E, int D, int G>
 hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 float scale, float alpha, const int32_t *sel,
-                                const int32_t *count, void *ws,
-                                hipStream_t stream);
+                                const int32_t *count, const float *tau_hint,
+                                void *ws, hipStream_t stream);
 template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,

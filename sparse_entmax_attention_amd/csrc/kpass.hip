@@ -3,6 +3,15 @@
 // every selected page and query head, each page's maximum per head, and the
 // page's pool slot, for the threshold and apply steps of decode.hip.  Reads
 // the selected keys once; HBM-bound.
+//
+// With a threshold hint per query head (the Gaussian selector's estimate
+// tau_hat), only the scores above f = hint - kHintMargin are written: each
+// page's candidates are packed at the start of the page's own score range, in
+// token order, and a 64-bit mask per page and head records which tokens they
+// are.  Scores at or below f cannot be in the support as long as tau >= f,
+// which the threshold step checks from the candidates themselves
+// (sum (z - f)_+^r >= 1 over them implies tau >= f).  Without a hint (f =
+// -inf) every valid token is a candidate and the layout is the plain one.
 #include <float.h>
 
 #include <type_traits>
@@ -24,20 +33,45 @@ namespace ekv {
 // exact and the wait for one group never waits for the groups behind it.
 constexpr int kKRing = 4;
 
+// Score floor of query head ug from the hint: hint - kHintMargin, or -inf
+// without a hint (or for a NaN hint).  The threshold step reads the value
+// stored by block 0 of the key pass, computed by this same function.
+__device__ __forceinline__ float hint_floor(const float *tau_hint, int ug) {
+  if (!tau_hint) return -INFINITY;
+  const float t = tau_hint[ug];
+  return t == t ? t - kHintMargin : -INFINITY;
+}
+
+// Block 0 records, for the threshold step, every head's score floor and its
+// query scaled by (alpha-1) scale (used to recompute scores when a hint
+// proves too high), and clears the count of heads left to the apply step.
+template <int D>
+__device__ __forceinline__ void record_heads(const float *q, const float *tau_hint,
+                                             float zscale, int n_heads,
+                                             float *floor_ws, float *qz,
+                                             int32_t *undone) {
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) *undone = 0;
+  for (int i = threadIdx.x; i < n_heads; i += blockDim.x)
+    floor_ws[i] = hint_floor(tau_hint, i);
+  for (int i = threadIdx.x; i < n_heads * D; i += blockDim.x) qz[i] = q[i] * zscale;
+}
+
 template <int D, int G, int P, bool SEL>
 __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
     const uint16_t *__restrict__ kpool, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ count, const float *__restrict__ q,
-    float zscale, int units, int H, int max_pages, int cap,
-    float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
+    const float *__restrict__ tau_hint, float zscale, int units, int H,
+    int max_pages, int cap, float *__restrict__ zbuf, float *__restrict__ pmax,
+    int32_t *__restrict__ slots, int32_t *__restrict__ undone,
+    float *__restrict__ floor_ws, float *__restrict__ qz,
+    unsigned long long *__restrict__ pmask) {
   constexpr int KS = D / 32;            // k-steps of 32 coordinates
   constexpr int NPASS = (G + 3) / 4;    // groups of 4 query heads
   constexpr int NT16 = P / 16;          // 16-token groups per page
   constexpr int U = kKRing / NT16;      // pages per body
-  // the threshold step counts the heads it leaves to the apply step
-  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
+  record_heads<D>(q, tau_hint, zscale, units * G, floor_ws, qz, undone);
   static_assert(kKRing % NT16 == 0, "a body holds whole pages");
   __shared__ int pref[kMaxUnits + 1];
   __shared__ int tmp[kDecWaves];
@@ -62,6 +96,9 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
 
   bf16x8_t a[NPASS][KS];
   bf16x8_t ring[kKRing][KS];
+  float flo[NPASS];                 // score floor of this lane's head 4 ps + kb
+  int run[NPASS];                   // candidates so far in the page, per head
+  unsigned long long pbits[NPASS];  // the page's candidate mask, per head
   int cur_u = -1;
   for (int c0 = f0; c0 < f1; c0 += kWave) {
     const int nc = min(kWave, f1 - c0);        // pages in this chunk
@@ -97,11 +134,19 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           if (u != cur_u) {  // rare: the run enters another unit
             cur_u = u;
             load_q_parts<D, G>(a, q, u / H, h, H, zscale);
+#pragma unroll
+            for (int ps = 0; ps < NPASS; ++ps) {
+              const int g = 4 * ps + kb;
+              flo[ps] = g < G ? hint_floor(tau_hint, u * G + g) : -INFINITY;
+            }
           }
 #pragma unroll
-          for (int ps = 0; ps < NPASS; ++ps)
+          for (int ps = 0; ps < NPASS; ++ps) {
+            run[ps] = 0;
+            pbits[ps] = 0ull;
 #pragma unroll
             for (int e = 0; e < 4; ++e) pm[ps][e] = -FLT_MAX;
+          }
         }
         const bool valid = 16 * tt + n < lane_val(rnt, ic);
         const __amdgpu_buffer_rsrc_t zr = store_rsrc(
@@ -127,9 +172,19 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
             if (valid) pm[ps][e] = fmaxf(pm[ps][e], z);
             zmine = kb == e ? z : zmine;
           }
+          // Candidates (z above the head's floor) go to the next free entry
+          // of the page's range; without a hint every valid token is one, at
+          // its own position, and the invalid tail keeps -inf as before.
           const int g = 4 * ps + kb;
-          store_if(zr, 4 * (g * cap + j * P + 16 * tt + n), g < G && live,
-                   valid ? zmine : -INFINITY);
+          const bool cand = valid && zmine > flo[ps];
+          const unsigned long long ball = __ballot(cand);
+          const unsigned gb = static_cast<unsigned>(ball >> (16 * kb)) & 0xffffu;
+          const int rank = run[ps] + __popc(gb & ((1u << n) - 1u));
+          const bool keep = cand || (!valid && flo[ps] == -INFINITY);
+          store_if(zr, 4 * (g * cap + j * P + (cand ? rank : 16 * tt + n)),
+                   keep && g < G && live, valid ? zmine : -INFINITY);
+          run[ps] += __popc(gb);
+          pbits[ps] |= static_cast<unsigned long long>(gb) << (16 * tt);
         }
         if (tt == NT16 - 1) {
           // the page's maxima, lane g holding head g's
@@ -150,6 +205,19 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
               pmax + static_cast<size_t>(u) * G * ps_,
               static_cast<size_t>(G) * ps_ * sizeof(float));
           store_if(pr, 4 * (lane * ps_ + j), lane < G && live, mine);
+          // candidate masks: lane 16 e of pass ps writes head 4 ps + e's
+          const __amdgpu_buffer_rsrc_t mr = store_rsrc(
+              pmask + static_cast<size_t>(u) * G * ps_,
+              static_cast<size_t>(G) * ps_ * sizeof(unsigned long long));
+#pragma unroll
+          for (int ps = 0; ps < NPASS; ++ps) {
+            typedef unsigned v2u __attribute__((ext_vector_type(2)));
+            const int g = 4 * ps + kb;
+            const v2u w = {static_cast<unsigned>(pbits[ps]),
+                           static_cast<unsigned>(pbits[ps] >> 32)};
+            __builtin_amdgcn_raw_buffer_store_b64(
+                w, mr, (n == 0 && g < G && live) ? 8 * (g * ps_ + j) : kDropOffset, 0, 0);
+          }
           const __amdgpu_buffer_rsrc_t sr = store_rsrc(
               slots + static_cast<size_t>(u) * max_pages,
               static_cast<size_t>(max_pages) * sizeof(int32_t));
@@ -175,8 +243,10 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
     const int32_t *__restrict__ count, const float *__restrict__ q,
     float zscale, int units, int H, int P, int max_pages, int cap,
     float *__restrict__ zbuf, float *__restrict__ pmax,
-    int32_t *__restrict__ slots, int32_t *__restrict__ undone) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
+    int32_t *__restrict__ slots, int32_t *__restrict__ undone,
+    float *__restrict__ floor_ws, float *__restrict__ qz) {
+  // float32 keys: every score is written (no hint is used)
+  record_heads<D>(q, nullptr, zscale, units * G, floor_ws, qz, undone);
   constexpr int LPT = D / 8;
   constexpr int TPW = kWave / LPT;
   __shared__ int pref[kMaxUnits + 1];
@@ -229,8 +299,8 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_valu(
 template <class E, int D, int G>
 hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 float scale, float alpha, const int32_t *sel,
-                                const int32_t *count, void *ws,
-                                hipStream_t stream) {
+                                const int32_t *count, const float *tau_hint,
+                                void *ws, hipStream_t stream) {
   const DecodeWs L = decode_ws_layout(kv);
   char *w = static_cast<char *>(ws);
   const int units = kv.batch * kv.num_kv_heads;
@@ -241,6 +311,9 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
   float *pm = reinterpret_cast<float *>(w + L.cmax);
   int32_t *sl = reinterpret_cast<int32_t *>(w + L.slot);
   int32_t *und = reinterpret_cast<int32_t *>(w + L.ctr) + units;
+  float *fl = reinterpret_cast<float *>(w + L.floor);
+  float *qz = reinterpret_cast<float *>(w + L.qz);
+  auto *mk = reinterpret_cast<unsigned long long *>(w + L.mask);
   const float zs = (alpha - 1.0f) * scale;
   if constexpr (sizeof(typename E::T) == 2) {
     const uint16_t *k = static_cast<const uint16_t *>(kv.k);
@@ -249,8 +322,9 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
       const int nb = resident_blocks(kern, kDecThreads,
                                      (pages + kDecWaves - 1) / kDecWaves);
       hipLaunchKernelGGL(kern, dim3(nb), dim3(kDecThreads), 0, stream, k,
-                         kv.page_table, kv.seq_lens, sel, count, q, zs, units,
-                         kv.num_kv_heads, kv.max_pages, cap, z, pm, sl, und);
+                         kv.page_table, kv.seq_lens, sel, count, q, tau_hint,
+                         zs, units, kv.num_kv_heads, kv.max_pages, cap, z, pm,
+                         sl, und, fl, qz, mk);
     };
     auto by_page = [&](auto has_sel) {
       constexpr bool S = decltype(has_sel)::value;
@@ -267,7 +341,8 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                        dim3(kDecThreads), 0, stream,
                        static_cast<const typename E::T *>(kv.k), kv.page_table,
                        kv.seq_lens, sel, count, q, zs, units, kv.num_kv_heads,
-                       kv.page_size, kv.max_pages, cap, z, pm, sl, und);
+                       kv.page_size, kv.max_pages, cap, z, pm, sl, und, fl,
+                       qz);
   }
   return hipGetLastError();
 }
@@ -275,7 +350,7 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
 #define EKV_INST_KPASS(E, D, G)                                              \
   template hipError_t launch_entmax_scores<E, D, G>(                         \
       const ekv_paged_kv &, const float *, float, float, const int32_t *,    \
-      const int32_t *, void *, hipStream_t);
+      const int32_t *, const float *, void *, hipStream_t);
 EKV_FOR_EACH_EDG(EKV_INST_KPASS)
 
 }  // namespace ekv

@@ -87,11 +87,12 @@ class DecodeBuffers:
                            self.count, self.tau_hat, self.ws_gauss, stream)
 
     def entmax(self, q, alpha: float, selected: bool = True, probs=None,
-               stream=None):
+               stream=None, tau_hint=None):
         B.ekv_entmax_decode(self.kv, q, self.scale, alpha,
                             self.sel if selected else None,
                             self.count if selected else None, self.out,
-                            self.tau, probs, self.ws_decode, stream)
+                            self.tau, probs, self.ws_decode, stream,
+                            tau_hint=tau_hint)
 
     def softmax(self, q, selected: bool = False, stream=None):
         B.ekv_softmax_decode(self.kv, q, self.scale,
@@ -105,7 +106,12 @@ class DecodeBuffers:
         self.select_topk(k, stream)
         self.entmax(q, alpha, True, None, stream)
 
-    def step_gauss(self, q, alpha: float, delta: float, stream=None):
+    def step_gauss(self, q, alpha: float, delta: float, stream=None,
+                   hint: bool = True):
+        """Gaussian selection, then entmax over the kept pages with the
+        selector's threshold estimates as the decode's hint (``hint=False``
+        decodes without it)."""
         self.score(q, B.EKV_SCORE_GAUSS, stream)
         self.select_gauss(alpha, delta, stream)
-        self.entmax(q, alpha, True, None, stream)
+        self.entmax(q, alpha, True, None, stream,
+                    tau_hint=self.tau_hat if hint else None)

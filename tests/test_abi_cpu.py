@@ -113,17 +113,22 @@ def test_validation_errors(lib):
     # decode: misaligned K, sel without count, non-positive scale, no output
     ws = 1 << 34
     assert lib.ekv_entmax_decode(ctypes.byref(_kv(k=FAKE + 2)), FAKE, 0.1, 1.5,
-                                 None, None, FAKE, None, None, FAKE, ws,
+                                 None, None, None, FAKE, None, None, FAKE, ws,
                                  None) == B.EKV_ERR_INVALID_ARG
     assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.1, 1.5, FAKE, None,
-                                 FAKE, None, None, FAKE, ws,
+                                 None, FAKE, None, None, FAKE, ws,
                                  None) == B.EKV_ERR_INVALID_ARG
     assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.0, 1.5, None, None,
-                                 FAKE, None, None, FAKE, ws,
+                                 FAKE, FAKE, None, None, FAKE, ws,
                                  None) == B.EKV_ERR_INVALID_ARG
     assert lib.ekv_entmax_decode(ctypes.byref(kv), FAKE, 0.1, 1.5, None, None,
-                                 None, None, None, FAKE, ws,
+                                 None, None, None, None, FAKE, ws,
                                  None) == B.EKV_ERR_INVALID_ARG
+    # the decode without a workspace refuses a cache beyond its static scratch
+    big = _kv(page_size=64, max_pages=16384)  # 1M tokens: 128 MiB of scores
+    assert lib.ekv_entmax_decode_noalloc(ctypes.byref(big), FAKE, 0.1, 1.5, None,
+                                         None, None, FAKE, None, None,
+                                         None) == B.EKV_ERR_WORKSPACE
     assert lib.ekv_softmax_decode(ctypes.byref(kv), FAKE, 0.1, None, None,
                                   FAKE, None, FAKE, 16,
                                   None) == B.EKV_ERR_WORKSPACE

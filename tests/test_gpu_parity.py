@@ -283,12 +283,19 @@ def test_selection_covering_support_matches_full_cache(gpu):
     torch.cuda.synchronize()
     assert torch.equal(sparse[1], buf.tau)
     assert torch.equal(sparse[0], buf.out)
-    buf.step_gauss(inp.q, 1.5, math.inf)
+    buf.step_gauss(inp.q, 1.5, math.inf, hint=False)
     torch.cuda.synchronize()
     P = inp.spec.page_size
     for b in range(inp.spec.batch):
         assert (buf.count[b] == (inp.lens[b] + P - 1) // P).all()
     assert torch.equal(sparse[0], buf.out)
+    # with the selector's threshold estimate as the hint the support sums run
+    # in another order: equal up to float rounding
+    buf.step_gauss(inp.q, 1.5, math.inf)
+    torch.cuda.synchronize()
+    assert torch.allclose(buf.tau, sparse[1], rtol=0, atol=1e-5)
+    assert (torch.linalg.vector_norm(buf.out - sparse[0], dim=-1)
+            <= 1e-5 * torch.linalg.vector_norm(sparse[0], dim=-1)).all()
 
 
 def test_determinism_and_slot_permutation(gpu):
