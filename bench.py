@@ -136,7 +136,7 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=-1,
                     help="(sequence, KV head) units the oracle is timed on; "
                          "-1 (default) all units of one step, 0 skips")
-    ap.add_argument("--legs", default="gauss,topk,entmax_full,softmax_full")
+    ap.add_argument("--legs", default="gauss,topk,topk_split,entmax_full,softmax_full")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: time the top-k and "
                          "Gaussian steps on prefixes of the workload's "
@@ -221,6 +221,22 @@ def main():
     dev_ev.close()
 
     # Each leg is a list of (phase name, callable).
+    n_keep = min(k_top, inp.max_pages)
+    topk_front = [
+        # box scoring is short enough that the in-kernel refresh (one wave's
+        # chain of loads) would lengthen it: two launches here
+        ("meta_tail", lambda: buf.build_meta(tail, span_hint=1)),
+        ("score_bbox", lambda: buf.score(q, ekv.EKV_SCORE_BBOX)),
+        ("select_topk", lambda: buf.select_topk(k_top)),
+    ]
+    split_decode = [
+        ("entmax_scores", lambda: ekv.ekv_entmax_scores(
+            kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
+        ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
+            kv, alpha, buf.sel, buf.count, buf.tau, buf.out, buf.ws_decode)),
+        ("entmax_apply", lambda: ekv.ekv_entmax_apply(
+            kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
+    ]
     legs = {
         "gauss": [
             # the tail page's metadata refresh runs inside the scoring launch
@@ -235,19 +251,13 @@ def main():
             ("entmax_apply", lambda: ekv.ekv_entmax_apply(
                 kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
         ],
-        "topk": [
-            # box scoring is short enough that the in-kernel refresh (one
-            # wave's chain of loads) would lengthen it: two launches here
-            ("meta_tail", lambda: buf.build_meta(tail, span_hint=1)),
-            ("score_bbox", lambda: buf.score(q, ekv.EKV_SCORE_BBOX)),
-            ("select_topk", lambda: buf.select_topk(k_top)),
-            ("entmax_scores", lambda: ekv.ekv_entmax_scores(
-                kv, q, buf.scale, alpha, buf.sel, buf.count, buf.ws_decode)),
-            ("entmax_threshold", lambda: ekv.ekv_entmax_threshold(
-                kv, alpha, buf.sel, buf.count, buf.tau, buf.out, buf.ws_decode)),
-            ("entmax_apply", lambda: ekv.ekv_entmax_apply(
-                kv, alpha, buf.sel, buf.count, buf.out, None, buf.ws_decode)),
-        ],
+        # top-k: the k pages' decode in one launch when they fit on chip
+        # (the split decode otherwise); "topk_split" always takes the split
+        # decode (key pass, threshold step), for comparison
+        "topk": topk_front + ([
+            ("entmax_small", lambda: buf.entmax_small(q, alpha, n_keep)),
+        ] if buf.small_fits(n_keep) else split_decode),
+        "topk_split": topk_front + split_decode,
         "entmax_full": [
             ("entmax_scores", lambda: ekv.ekv_entmax_scores(
                 kv, q, buf.scale, alpha, None, None, buf.ws_decode)),
@@ -402,7 +412,7 @@ def main():
         warm = args.warmup
         log("[bench] leg %s: %d warmup + %d timed steps" % (name, warm, steps))
         r = run_leg(name, steps, warm)
-        if name in ("gauss", "topk"):
+        if name in ("gauss", "topk", "topk_split"):
             pages, toks = selection_stats()
             # what the selection costs each attention (same pages for both),
             # measured after the timed steps from the selection they left
@@ -427,8 +437,16 @@ def main():
                 "score_gauss" if name == "gauss" else "score_bbox":
                     mbytes + n_pages_total * H * G * (8 if name == "gauss" else 4) +
                     (tail_bytes if name == "gauss" else 0),
-                "entmax_scores": kbytes + sel_positions * G * 4,
+                # the key pass reads the selected keys; unhinted it writes
+                # every score, hinted only those near the support (a few
+                # hundred per head: left out)
+                "entmax_scores": kbytes + (0 if name == "gauss" else sel_positions * G * 4),
             }
+            if "entmax_small" in r["phase_ms"]:
+                # keys of the selection and value rows of the support read,
+                # the output rows written
+                rbytes = B * H * G * D * 4
+                r["kernel_bytes"]["entmax_small"] = kbytes + vbytes + rbytes
         elif name == "entmax_full":
             rows = support_rows(False)
             kbytes = tokens_total * H * D * e
@@ -450,7 +468,7 @@ def main():
     head = results.get("gauss") or next(iter(results.values()))
     head_name = "gauss" if "gauss" in results else next(iter(results))
     # Dominant kernel of the headline step and its roofline.
-    kb = head["kernel_bytes"]
+    kb = {k: v for k, v in head["kernel_bytes"].items() if k in head["phase_ms"]}
     dom = max(kb, key=lambda kname: head["phase_ms"][kname])
     # Its duration without an event around it: the step cut just after the
     # kernel minus the step cut just before it, each timed like the headline
@@ -480,9 +498,10 @@ def main():
         if base in results and head_name in results:
             speedups["%s_over_%s" % (head_name, base)] = round(
                 results[base]["median_ms"] / head["median_ms"], 3)
-        if base in results and "topk" in results:
-            speedups["topk_over_%s" % base] = round(
-                results[base]["median_ms"] / results["topk"]["median_ms"], 3)
+        for tk in ("topk", "topk_split"):
+            if base in results and tk in results:
+                speedups["%s_over_%s" % (tk, base)] = round(
+                    results[base]["median_ms"] / results[tk]["median_ms"], 3)
 
     cpu, cpu_more = None, None
     n_cpu = B * H if args.cpu_units < 0 else args.cpu_units

@@ -75,6 +75,7 @@ typedef enum ekv_dtype {
 #define EKV_OP_SELECT_GAUSS 2
 #define EKV_OP_ENTMAX_DECODE 3
 #define EKV_OP_SOFTMAX_DECODE 4
+#define EKV_OP_ENTMAX_DECODE_SMALL 5
 
 /*
  * Paged KV cache (Technical Summary, §2 and §2.A: the cache is cut into
@@ -274,6 +275,36 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
                                      const int32_t *sel, const int32_t *count,
                                      const float *tau_hint, float *out,
                                      float *tau, float *probs, void *stream);
+
+/*
+ * ekv_entmax_decode_small - ekv_entmax_decode in a single launch for small
+ * selections (Technical Summary, §2.B.1 and §2.C: a fixed budget of k pages
+ * per unit).  Blocks share each unit's selection: they gather its keys
+ * through the page table and compute z for the unit's G query heads; the
+ * last block to finish solves each head's tau exactly (alpha in {1.5, 2};
+ * bisection otherwise) and sums the value rows of the support.  Scores stay
+ * on chip when one block takes a unit (many units); otherwise they pass
+ * through the workspace once.
+ *   sel, count   as for ekv_entmax_decode (sel == NULL: every page).
+ *   max_count    an upper bound on every unit's page count (for top-k
+ *                selections: min(k, max_pages)), 1 <= max_count and
+ *                max_count * page_size <= 2048 (EKV_ERR_INVALID_ARG below
+ *                1, EKV_ERR_UNSUPPORTED above 2048 tokens).  A unit whose
+ *                count exceeds max_count or max_pages gets NaN in its rows
+ *                of out and tau, and nothing past the bound is read.
+ *   out, tau     as for ekv_entmax_decode (tau nullable).
+ * bfloat16 keys only (EKV_ERR_UNSUPPORTED otherwise).
+ * Workspace: ekv_workspace_size(EKV_OP_ENTMAX_DECODE_SMALL, kv, max_count)
+ * bytes, 256-byte aligned.  Unlike the other workspaces it holds state: it
+ * must be zero-filled before its first use, and every call leaves it ready
+ * for the next (its arrival counters back at zero).  Calls that overlap in
+ * time must not share one.
+ */
+ekv_status ekv_entmax_decode_small(const ekv_paged_kv *kv, const float *q,
+                                   float scale, float alpha,
+                                   const int32_t *sel, const int32_t *count,
+                                   int32_t max_count, float *out, float *tau,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /*
  * The three steps of ekv_entmax_decode, for callers that time or interleave

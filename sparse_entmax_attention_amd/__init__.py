@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     EKV_RULE_HERMITE, EKV_RULE_JACOBI, EKV_SCORE_GAUSS, EkvError, LIB_PATH,
     PagedKV, ekv_build_meta, ekv_quadrature_rule,
     ekv_entmax_apply, ekv_entmax_decode, ekv_entmax_decode_noalloc,
+    ekv_entmax_decode_small,
     ekv_entmax_scores,
     EKV_READ_PROBE_SINK, ekv_entmax_threshold, ekv_read_probe,
     ekv_refresh_score_pages, ekv_score_pages, ekv_select_gauss,

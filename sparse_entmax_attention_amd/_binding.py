@@ -33,6 +33,7 @@ EKV_OP_SELECT_TOPK = 1
 EKV_OP_SELECT_GAUSS = 2
 EKV_OP_ENTMAX_DECODE = 3
 EKV_OP_SOFTMAX_DECODE = 4
+EKV_OP_ENTMAX_DECODE_SMALL = 5
 
 _c_i32 = ctypes.c_int32
 _c_f32 = ctypes.c_float
@@ -74,6 +75,9 @@ _SIGNATURES = {
     "ekv_entmax_decode_noalloc": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p,
                                            _c_f32, _c_f32, _c_p, _c_p, _c_p,
                                            _c_p, _c_p, _c_p, _c_p]),
+    "ekv_entmax_decode_small": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p,
+                                         _c_f32, _c_f32, _c_p, _c_p, _c_i32,
+                                         _c_p, _c_p, _c_p, _c_size, _c_p]),
     "ekv_entmax_scores": (_c_i32, [ctypes.POINTER(ekv_paged_kv), _c_p, _c_f32,
                                    _c_f32, _c_p, _c_p, _c_p, _c_p, _c_size,
                                    _c_p]),
@@ -272,6 +276,19 @@ def ekv_entmax_decode_noalloc(kv: PagedKV, q, scale: float, alpha: float, sel,
         _ptr(count), _ptr(tau_hint), _ptr(out), _ptr(tau), _ptr(probs),
         _stream(stream)),
         "ekv_entmax_decode_noalloc")
+
+
+def ekv_entmax_decode_small(kv: PagedKV, q, scale: float, alpha: float, sel,
+                            count, max_count: int, out, tau=None, ws=None,
+                            stream=None) -> None:
+    """ws: ekv_workspace_size(EKV_OP_ENTMAX_DECODE_SMALL, kv, max_count)
+    bytes, zero-filled before its first use (each call leaves it so)."""
+    s = kv.struct()
+    _check(load_library().ekv_entmax_decode_small(
+        ctypes.byref(s), _ptr(q), float(scale), float(alpha), _ptr(sel),
+        _ptr(count), int(max_count), _ptr(out), _ptr(tau), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)),
+        "ekv_entmax_decode_small")
 
 
 def ekv_entmax_scores(kv: PagedKV, q, scale: float, alpha: float, sel, count,

@@ -192,7 +192,6 @@ ekv_status scratch_on(hipStream_t stream, void **ptr) {
 extern "C" {
 
 size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
-  (void)k_or_0;
   if (check_kv(kv, false, false) != EKV_OK) return 0;
   const size_t units = static_cast<size_t>(kv->batch) * kv->num_kv_heads;
   switch (op) {
@@ -206,6 +205,8 @@ size_t ekv_workspace_size(int32_t op, const ekv_paged_kv *kv, int32_t k_or_0) {
       return ekv::decode_ws_layout(*kv).total;
     case EKV_OP_SOFTMAX_DECODE:
       return ekv::softmax_ws_layout(*kv).total;
+    case EKV_OP_ENTMAX_DECODE_SMALL:  // k_or_0: max_count
+      return k_or_0 >= 1 ? ekv::small_ws_bytes(*kv, k_or_0) : 0;
     default:
       return 0;
   }
@@ -404,6 +405,33 @@ ekv_status ekv_entmax_decode_noalloc(const ekv_paged_kv *kv, const float *q,
   EKV_TRY(scratch_on(as_stream(stream), &ws));
   return ekv_entmax_decode(kv, q, scale, alpha, sel, count, tau_hint, out, tau,
                            probs, ws, kScratchBytes, stream);
+}
+
+ekv_status ekv_entmax_decode_small(const ekv_paged_kv *kv, const float *q,
+                                   float scale, float alpha,
+                                   const int32_t *sel, const int32_t *count,
+                                   int32_t max_count, float *out, float *tau,
+                                   void *ws, size_t ws_bytes, void *stream) {
+  EKV_TRY(check_kv(kv, true, true));
+  EKV_TRY(check_scale(scale));
+  EKV_TRY(check_alpha(alpha));
+  EKV_TRY(check_sel(sel, count));
+  if (!q || !aligned(q, 16) || !out)
+    return fail(EKV_ERR_INVALID_ARG, "q (16-byte aligned) and out are required");
+  if (kv->kv_dtype != EKV_BF16)
+    return fail(EKV_ERR_UNSUPPORTED, "the small-selection decode is built for bfloat16 keys");
+  if (max_count < 1)
+    return fail(EKV_ERR_INVALID_ARG, "max_count must be >= 1 (got %d)", max_count);
+  if (static_cast<long long>(max_count) * kv->page_size > ekv::kSmallTokens)
+    return fail(EKV_ERR_UNSUPPORTED,
+                "max_count %d * page_size %d exceeds the %d tokens held on chip",
+                max_count, kv->page_size, ekv::kSmallTokens);
+  EKV_TRY(check_ws(ws, ws_bytes, ekv::small_ws_bytes(*kv, max_count)));
+  const hipError_t e = with_edg(*kv, [&](auto, auto D, auto G) {
+    return ekv::launch_entmax_small<decltype(D)::value, decltype(G)::value>(
+        *kv, q, scale, alpha, sel, count, max_count, out, tau, ws, as_stream(stream));
+  });
+  return hip_status(e, "ekv_entmax_decode_small launch");
 }
 
 ekv_status ekv_softmax_decode(const ekv_paged_kv *kv, const float *q,

@@ -79,6 +79,17 @@ hipError_t launch_entmax_scores(const ekv_paged_kv &kv, const float *q,
                                 float scale, float alpha, const int32_t *sel,
                                 const int32_t *count, const float *tau_hint,
                                 void *ws, hipStream_t stream);
+// Tokens of one unit the single-launch small-selection decode holds on chip.
+constexpr int kSmallTokens = 2048;
+
+template <int D, int G>
+hipError_t launch_entmax_small(const ekv_paged_kv &kv, const float *q,
+                               float scale, float alpha, const int32_t *sel,
+                               const int32_t *count, int max_count, float *out,
+                               float *tau, void *ws, hipStream_t stream);
+// Workspace of the small-selection decode: per-unit arrival counters, then
+// the units' scores.
+size_t small_ws_bytes(const ekv_paged_kv &kv, int max_count);
 template <class E, int D, int G>
 hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
                                    const int32_t *sel, const int32_t *count,

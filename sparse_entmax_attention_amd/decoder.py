@@ -13,6 +13,8 @@ import torch
 
 from . import _binding as B
 
+SMALL_TOKENS = 2048  # tokens per unit the single-launch decode holds on chip
+
 
 class DecodeBuffers:
     """Outputs and workspaces of one paged cache's decode step.
@@ -50,6 +52,7 @@ class DecodeBuffers:
         self.ws_gauss = self._ws(B.EKV_OP_SELECT_GAUSS)
         self.ws_decode = self._ws(B.EKV_OP_ENTMAX_DECODE)
         self.ws_softmax = self._ws(B.EKV_OP_SOFTMAX_DECODE) if softmax else None
+        self.ws_small = None  # grown on demand, zero-filled (it holds counters)
 
     def _ws(self, op: int) -> Optional[torch.Tensor]:
         n = B.ekv_workspace_size(op, self.kv, 1)
@@ -94,6 +97,21 @@ class DecodeBuffers:
                             self.tau, probs, self.ws_decode, stream,
                             tau_hint=tau_hint)
 
+    def entmax_small(self, q, alpha: float, max_count: int, selected: bool = True,
+                     stream=None):
+        n = B.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE_SMALL, self.kv, max_count)
+        if self.ws_small is None or self.ws_small.numel() < n:
+            self.ws_small = torch.zeros(n, dtype=torch.uint8, device=self.kv.device)
+        B.ekv_entmax_decode_small(self.kv, q, self.scale, alpha,
+                                  self.sel if selected else None,
+                                  self.count if selected else None, max_count,
+                                  self.out, self.tau, self.ws_small, stream)
+
+    def small_fits(self, max_count: int) -> bool:
+        """Whether the single-launch decode takes selections of max_count pages."""
+        return (self.kv.k.dtype == torch.bfloat16 and
+                max_count * self.kv.page_size <= SMALL_TOKENS)
+
     def softmax(self, q, selected: bool = False, stream=None):
         B.ekv_softmax_decode(self.kv, q, self.scale,
                              self.sel if selected else None,
@@ -101,10 +119,19 @@ class DecodeBuffers:
                              self.lse, self.ws_softmax, stream)
 
     # -- whole steps ---------------------------------------------------------
-    def step_topk(self, q, alpha: float, k: int, stream=None):
+    def step_topk(self, q, alpha: float, k: int, stream=None, small=None):
+        """Box scoring, top-k selection, then entmax over the kept pages: in
+        one launch when the k pages fit on chip (``small``: None chooses,
+        False forces the split decode)."""
         self.score(q, B.EKV_SCORE_BBOX, stream)
         self.select_topk(k, stream)
-        self.entmax(q, alpha, True, None, stream)
+        n_keep = min(k, self.kv.max_pages)
+        if small is None:
+            small = self.small_fits(n_keep)
+        if small:
+            self.entmax_small(q, alpha, n_keep, True, stream)
+        else:
+            self.entmax(q, alpha, True, None, stream)
 
     def step_gauss(self, q, alpha: float, delta: float, stream=None,
                    hint: bool = True):

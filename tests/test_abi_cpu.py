@@ -69,6 +69,11 @@ def test_workspace_sizes(lib):
     gauss = lib.ekv_workspace_size(B.EKV_OP_SELECT_GAUSS, ctypes.byref(kv), 0)
     assert gauss == units * G * ((1024 + 63) // 64) * 8  # page mask per head and tile
     assert lib.ekv_workspace_size(99, ctypes.byref(kv), 0) == 0
+    # small-selection decode: 256 bytes of arrival counters (8 units), then
+    # the scores of max_count pages for every query head
+    small = lib.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE_SMALL, ctypes.byref(kv), 16)
+    assert small == 256 + units * G * 16 * 32 * 4
+    assert lib.ekv_workspace_size(B.EKV_OP_ENTMAX_DECODE_SMALL, ctypes.byref(kv), 0) == 0
     # score buffers: per-page values plus 64-page tile summaries
     T = (1024 + 63) // 64
     assert lib.ekv_score_size(ctypes.byref(kv), B.EKV_SCORE_BBOX) == 32 * 1024 + 8 * T
@@ -129,6 +134,22 @@ def test_validation_errors(lib):
     assert lib.ekv_entmax_decode_noalloc(ctypes.byref(big), FAKE, 0.1, 1.5, None,
                                          None, None, FAKE, None, None,
                                          None) == B.EKV_ERR_WORKSPACE
+    # the single-launch decode: max_count >= 1, at most 2048 tokens on chip,
+    # bfloat16 keys
+    def small(kv_, max_count, out=FAKE):
+        return lib.ekv_entmax_decode_small(ctypes.byref(kv_), FAKE, 0.1, 1.5,
+                                           FAKE, FAKE, max_count, out, None,
+                                           FAKE, 1 << 30, None)
+    assert small(kv, 0) == B.EKV_ERR_INVALID_ARG
+    assert small(kv, 65) == B.EKV_ERR_UNSUPPORTED  # 65 pages of 32 tokens
+    assert small(_kv(kv_dtype=B.EKV_F32), 16) == B.EKV_ERR_UNSUPPORTED
+    assert small(kv, 16, out=None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_entmax_decode_small(ctypes.byref(kv), FAKE, 0.1, 1.0, FAKE,
+                                       FAKE, 16, FAKE, None, FAKE, 1 << 30,
+                                       None) == B.EKV_ERR_INVALID_ARG
+    assert lib.ekv_entmax_decode_small(ctypes.byref(kv), FAKE, 0.1, 1.5, FAKE,
+                                       FAKE, 16, FAKE, None, FAKE, 16,
+                                       None) == B.EKV_ERR_WORKSPACE
     assert lib.ekv_softmax_decode(ctypes.byref(kv), FAKE, 0.1, None, None,
                                   FAKE, None, FAKE, 16,
                                   None) == B.EKV_ERR_WORKSPACE

@@ -127,13 +127,17 @@ def test_page_scores(gpu, name):
                                     ("cluster_p64", 200), ("gqa8_d128", 40),
                                     ("gqa2_d64_p16", 64)])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
-def test_topk_decode(gpu, name, k, alpha):
+@pytest.mark.parametrize("path", ["auto", "split"])
+def test_topk_decode(gpu, name, k, alpha, path):
+    # "auto": the single-launch decode wherever the k pages fit on chip
+    # (bfloat16, k * P <= 2048), else the split decode; "split": always the
+    # split decode (key pass, threshold step)
     inp, host = inputs(name, gpu)
     spec = inp.spec
     kv = paged_kv(inp)
     buf = ekv.DecodeBuffers(kv)
     buf.build_meta()
-    buf.step_topk(inp.q, alpha, k)
+    buf.step_topk(inp.q, alpha, k, small=None if path == "auto" else False)
     torch.cuda.synchronize()
     sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
     tau, out = f64(buf.tau), f64(buf.out)
@@ -601,3 +605,39 @@ def test_gauss_threshold_general_alpha_both_rules(gpu, alpha):
     for j in range(G):
         assert abs(tau[0, j] - ref["tau"][j]) <= TAU_ATOL
         assert rel_l2(out[0, j], ref["out"][j]) <= OUT_RTOL_L2
+
+
+def test_small_decode_guards_and_full_cache(gpu):
+    # the single-launch decode: NaN rows for a unit whose selection exceeds
+    # the promised bound, the full cache of a short sequence (sel = NULL),
+    # and run-to-run bit equality
+    spec = workloads.workload("cluster_128k_b4", batch=2, seq_len=1500)
+    print("[case] small decode guards, seed 120", flush=True)
+    inp = workloads.generate(spec, 120, gpu)
+    host = HostCopy(inp)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    buf.score(inp.q, ekv.EKV_SCORE_BBOX)
+    buf.select_topk(6)
+    buf.entmax_small(inp.q, 1.5, 5)  # 6 pages kept, 5 promised
+    torch.cuda.synchronize()
+    assert torch.isnan(buf.out).all() and torch.isnan(buf.tau).all()
+    n_pages = (1500 + spec.page_size - 1) // spec.page_size
+    for alpha in (1.5, 2.0, 1.25):
+        buf.entmax_small(inp.q, alpha, n_pages, selected=False)
+        torch.cuda.synchronize()
+        tau, out = f64(buf.tau), f64(buf.out)
+        G, sc = spec.group, scale_of(spec)
+        for b, h in _units(inp):
+            qs, keys, vals = host.unit(b, h)
+            for j in range(G):
+                z = (alpha - 1) * O.token_scores(qs[j], keys, sc)
+                t = O.entmax_threshold(z, alpha)
+                p = O.entmax_probs(z, t, alpha)
+                assert abs(tau[b, h * G + j] - t) <= TAU_ATOL
+                assert rel_l2(out[b, h * G + j], (p[:, None] * vals).sum(0)) <= OUT_RTOL_L2
+        again = buf.out.clone()
+        buf.entmax_small(inp.q, alpha, n_pages, selected=False)
+        torch.cuda.synchronize()
+        assert torch.equal(again, buf.out)
