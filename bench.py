@@ -180,7 +180,6 @@ def main():
     k_top = spec.topk or 16
     delta = spec.delta
     q = inp.q
-    tail = torch.tensor([(L - 1) // P for L in inp.lens], dtype=torch.int32, device=dev)
     if args.flush == "read":
         flush_buf = torch.ones(256 << 20, dtype=torch.float32, device=dev)  # 1 GiB
         flush = lambda s: torch.amax(flush_buf)
@@ -223,10 +222,8 @@ def main():
     # Each leg is a list of (phase name, callable).
     n_keep = min(k_top, inp.max_pages)
     topk_front = [
-        # box scoring is short enough that the in-kernel refresh (one wave's
-        # chain of loads) would lengthen it: two launches here
-        ("meta_tail", lambda: buf.build_meta(tail, span_hint=1)),
-        ("score_bbox", lambda: buf.score(q, ekv.EKV_SCORE_BBOX)),
+        # the tail page's box refresh runs inside the scoring launch
+        ("score_bbox", lambda: buf.refresh_score(q, ekv.EKV_SCORE_BBOX)),
         ("select_topk", lambda: buf.select_topk(k_top)),
     ]
     split_decode = [
@@ -373,10 +370,9 @@ def main():
             lens = [min(L, n) for n in full_lens]
             inp.lens[:] = lens
             inp.seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
-            tail.copy_(torch.tensor([(n - 1) // P for n in lens], dtype=torch.int32))
             n_pages = sum((n + P - 1) // P for n in lens)
             row = {"seq_len": L}
-            for name, sel_phases in (("topk", ("meta_tail", "score_bbox", "select_topk")),
+            for name, sel_phases in (("topk", ("score_bbox", "select_topk")),
                                      ("gauss", ("score_gauss", "select_gauss"))):
                 r = run_leg(name, args.steps, args.warmup)
                 pages, toks = selection_stats()
@@ -430,13 +426,13 @@ def main():
                             "selected_k": kbytes, "support_v": vbytes})
             step_bytes = mbytes + tail_bytes + kbytes + vbytes
             sel_positions = pages * P
-            # scoring: metadata read and per-page values written; on the
-            # Gaussian leg the launch also refreshes the tail pages (keys of
-            # each sequence's last page read)
+            # scoring: metadata read and per-page values written; the launch
+            # also refreshes the tail pages (keys of each sequence's last
+            # page read)
             r["kernel_bytes"] = {
                 "score_gauss" if name == "gauss" else "score_bbox":
                     mbytes + n_pages_total * H * G * (8 if name == "gauss" else 4) +
-                    (tail_bytes if name == "gauss" else 0),
+                    tail_bytes,
                 # the key pass reads the selected keys; unhinted it writes
                 # every score, hinted only those near the support (a few
                 # hundred per head: left out)

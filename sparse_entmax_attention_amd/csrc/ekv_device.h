@@ -262,15 +262,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
+__device__ __forceinline__ int wave_incl_scan(int x) { return wave_incl_scan_dpp(x); }
 
 // Exclusive prefix sum over a block of NT threads; also returns the total.
 // `smem` must hold NT/64 ints.  Contains barriers: call from all threads.

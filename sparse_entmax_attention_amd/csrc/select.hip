@@ -29,6 +29,19 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Largest unsigned value over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(dpp_i<kDppRowMirror>(static_cast<int>(x))));
+  x = max(x, static_cast<uint32_t>(dpp_i<kDppRowHalfMirror>(static_cast<int>(x))));
+  x = max(x, static_cast<uint32_t>(dpp_i<kDppQuad2301>(static_cast<int>(x))));
+  x = max(x, static_cast<uint32_t>(dpp_i<kDppQuad1032>(static_cast<int>(x))));
+  x = max(x, static_cast<uint32_t>(dpp_rows<kDppRowBcast15, 0xA>(static_cast<int>(x),
+                                                                static_cast<int>(x))));
+  x = max(x, static_cast<uint32_t>(dpp_rows<kDppRowBcast31, 0xC>(static_cast<int>(x),
+                                                                static_cast<int>(x))));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), kWave - 1));
+}
+
 // Ordered list of the indices i < n with pred(i), written to out (at most
 // cap entries are stored); returns the count.  Rounds of one index per
 // thread; contains barriers.
@@ -46,29 +59,57 @@ __device__ int ordered_list(int n, F pred, int *out, int cap, int *tmp) {
   return total;
 }
 
-// kk-th largest of n keys key_at(i) (kk <= n): returns the key T and, in
-// need, how many keys equal to T belong to the kk largest.  Most
-// significant digit first, 8 bits per pass.  Contains barriers.
+// kk-th largest of n keys key_at(i) (kk <= n): returns the key T, in need
+// how many keys equal to T belong to the kk largest, and in n_at how many
+// keys equal T.  Most significant digit first, 8 bits per pass, from the
+// digit at bit shift_hi down to the one at shift_lo (the bits below shift_lo
+// are returned as 0, a lower bound of T); keys whose bits above shift_hi + 7
+// differ from prefix0 are left out (the caller knows every key of the kk
+// largest has them).  hist holds two 256-bin
+// histograms and s_digit / s_need (need, count) two slots, used in turn, so that a pass
+// needs two barriers: one after its histogram (then wave 0 finds the digit
+// while the other waves clear the next histogram), one after the digit.
+// A wave whose keys all share the digit adds them with one atomic.
+// Contains barriers.
 template <class F>
 __device__ uint32_t radix_select(F key_at, int n, int kk, int *hist,
-                                 uint32_t *s_digit, int *s_need, int &need) {
-  uint32_t prefix = 0, mask = 0;
+                                 uint32_t *s_digit, int *s_need, int &need,
+                                 int &n_at, int shift_hi = 24, int shift_lo = 0,
+                                 uint32_t prefix0 = 0u) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t mask = shift_hi >= 24 ? 0u : ~((256u << shift_hi) - 1u);
+  uint32_t prefix = prefix0 & mask;
   need = kk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
-    lds_barrier();
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+  for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+  lds_barrier();
+  int pass = 0;
+  n_at = 0;
+  for (int shift = shift_hi; shift >= shift_lo; shift -= 8, ++pass) {
+    int *hc = hist + 256 * (pass & 1), *hn = hist + 256 * ((pass + 1) & 1);
+    for (int base = 0; base < n; base += kSelThreads) {
+      const int i = base + threadIdx.x;
+      const uint32_t key = i < n ? key_at(i) : 0u;
+      const bool act = i < n && (key & mask) == prefix;
+      const uint32_t dg = (key >> shift) & 255u;
+      const unsigned long long on = __ballot(act);
+      if (on) {
+        const int first = __ffsll(static_cast<long long>(on)) - 1;
+        const uint32_t d0 = static_cast<uint32_t>(
+            __builtin_amdgcn_readlane(static_cast<int>(dg), first));
+        if ((__ballot(act && dg != d0)) == 0ull) {
+          if (lane == first) atomicAdd(&hc[d0], __popcll(on));
+        } else if (act) {
+          atomicAdd(&hc[dg], 1);
+        }
+      }
     }
     lds_barrier();
     if (threadIdx.x < kWave) {
       // Lane l owns digits 255-4l .. 252-4l (descending).
-      const int l = threadIdx.x;
       int c[4], local = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * l - j];
+        c[j] = hc[255 - 4 * lane - j];
         local += c[j];
       }
       const int incl = wave_incl_scan(local);
@@ -76,17 +117,20 @@ __device__ uint32_t radix_select(F key_at, int n, int kk, int *hist,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (before < need && before + c[j] >= need) {
-          *s_digit = static_cast<uint32_t>(255 - 4 * l - j);
-          *s_need = need - before;
+          s_digit[pass & 1] = static_cast<uint32_t>(255 - 4 * lane - j);
+          s_need[pass & 1] = need - before;
+          s_need[2 + (pass & 1)] = c[j];
         }
         before += c[j];
       }
+    } else {
+      for (int i = threadIdx.x - kWave; i < 256; i += kSelThreads - kWave) hn[i] = 0;
     }
     lds_barrier();
-    prefix |= *s_digit << shift;
+    prefix |= s_digit[pass & 1] << shift;
     mask |= 255u << shift;
-    need = *s_need;
-    lds_barrier();
+    need = s_need[pass & 1];
+    n_at = s_need[2 + (pass & 1)];
   }
   return prefix;
 }
@@ -114,10 +158,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
     int32_t *__restrict__ count, uint32_t *__restrict__ keys_ws) {
   __shared__ uint32_t s_keys[kTopkCand + kTopkCand / 16];
   __shared__ int s_tiles[kTopkTileCap];
-  __shared__ int hist[256];
+  __shared__ int hist[512];
   __shared__ int tmp[kSelWaves];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_need;
+  __shared__ uint32_t s_digit[2];
+  __shared__ int s_need[4];
+  __shared__ uint32_t s_wmax[kSelWaves];
   const int u = blockIdx.x, b = u / H, h = u % H;
   const int tid = threadIdx.x;
   const int np = n_pages_of(seq_lens[b], P);
@@ -145,12 +190,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
   // 1-2. candidate tiles and their pages
   int n_ct = nt;
   bool tiles_listed = false;
+  uint32_t T0 = 0u;
   if (nt > kk && nt <= kTopkTileCap) {
     for (int t = tid; t < nt; t += kSelThreads) s_keys[t] = order_key(ubt[t]);
     lds_barrier();
-    int nd;
-    const uint32_t T0 = radix_select([&](int i) { return s_keys[i]; }, nt, kk,
-                                     hist, &s_digit, &s_need, nd);
+    // T0 to 16 bits (rounded down): a few more tiles may reach it, all of
+    // the k best pages still do
+    int nd, nat;
+    T0 = radix_select([&](int i) { return s_keys[i]; }, nt, kk,
+                      hist, s_digit, s_need, nd, nat, 24, 16);
     n_ct = ordered_list(nt, [&](int t) { return s_keys[t] >= T0; }, s_tiles,
                         kTopkTileCap, tmp);
     tiles_listed = true;
@@ -165,6 +213,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
   const bool in_lds = n_slots <= kTopkCand;
   uint32_t *gkeys = keys_ws + static_cast<size_t>(u) * n_tiles * kPageTile;
   constexpr int KU = 4;
+  uint32_t kmax = 0u;
   for (int s0 = tid; s0 < n_slots; s0 += kSelThreads * KU) {
     uint32_t kv[KU];
 #pragma unroll
@@ -172,6 +221,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
       const int s = s0 + k2 * kSelThreads;
       const int p = s < n_slots ? page_of_slot(s) : np;
       kv[k2] = p < np ? page_key(p) : 0u;
+      kmax = max(kmax, kv[k2]);
     }
 #pragma unroll
     for (int k2 = 0; k2 < KU; ++k2) {
@@ -182,14 +232,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
       }
     }
   }
+  kmax = wave_max_u(kmax);
+  if ((tid & (kWave - 1)) == 0) s_wmax[tid / kWave] = kmax;
   if (in_lds) lds_barrier(); else __syncthreads();
   auto key_at = [&](int s) { return in_lds ? s_keys[pad16(s)] : gkeys[s]; };
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) kmax = max(kmax, s_wmax[w]);
 
-  // 3. k-th largest candidate, then the ordered compaction over slots.
-  int need;
-  const uint32_t T = radix_select(key_at, n_slots, kk, hist, &s_digit, &s_need, need);
+  // 3. k-th largest candidate, then the ordered compaction over slots.  The
+  // k best keys lie in [T0, kmax]: the digits those two share are skipped.
+  int shift_hi = 24;
+  while (shift_hi > 0 && ((T0 ^ kmax) >> shift_hi) == 0u) shift_hi -= 8;
+  int need, n_at;
+  const uint32_t T = radix_select(key_at, n_slots, kk, hist, s_digit, s_need,
+                                  need, n_at, shift_hi, 0, kmax);
   const int per = (n_slots + kSelThreads - 1) / kSelThreads;
   const int s_beg = tid * per, s_end = min(n_slots, s_beg + per);
+  if (n_at == need) {  // every key equal to T is taken: keys >= T, in order
+    int n_sel = 0;
+    for (int s = s_beg; s < s_end; ++s) n_sel += (key_at(s) >= T);
+    int tot;
+    int pos = block_excl_scan<kSelThreads>(n_sel, tmp, tot);
+    for (int s = s_beg; s < s_end; ++s)
+      if (key_at(s) >= T) out[pos++] = page_of_slot(s);
+    if (tid == 0) count[u] = kk;
+    return;
+  }
   int n_eq = 0;
   for (int s = s_beg; s < s_end; ++s) n_eq += (key_at(s) == T);
   int tot;
