@@ -136,7 +136,14 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=-1,
                     help="(sequence, KV head) units the oracle is timed on; "
                          "-1 (default) all units of one step, 0 skips")
-    ap.add_argument("--legs", default="gauss,topk,topk_split,entmax_full,softmax_full")
+    ap.add_argument("--legs", default="gauss,topk,topk_split,softmax_topk,entmax_full,softmax_full")
+    ap.add_argument("--extra", default="cluster_128k_b4,ragged_pool_b16",
+                    help="other workloads timed after the main legs (comma "
+                         "separated; empty for none): the Gaussian step on "
+                         "cluster_128k_b4, and on ragged_pool_b16 with one "
+                         "token appended per sequence per step")
+    ap.add_argument("--extra-steps", type=int, default=64)
+    ap.add_argument("--extra-warmup", type=int, default=8)
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: time the top-k and "
                          "Gaussian steps on prefixes of the workload's "
@@ -265,6 +272,11 @@ def main():
         ],
         "softmax_full": [
             ("softmax", lambda: buf.softmax(q)),
+        ],
+        # split-K softmax over the same top-k pages (the pages' softmax
+        # top-k comparison)
+        "softmax_topk": topk_front + [
+            ("softmax", lambda: buf.softmax(q, selected=True)),
         ],
     }
 
@@ -408,7 +420,7 @@ def main():
         warm = args.warmup
         log("[bench] leg %s: %d warmup + %d timed steps" % (name, warm, steps))
         r = run_leg(name, steps, warm)
-        if name in ("gauss", "topk", "topk_split"):
+        if name in ("gauss", "topk", "topk_split", "softmax_topk"):
             pages, toks = selection_stats()
             # what the selection costs each attention (same pages for both),
             # measured after the timed steps from the selection they left
@@ -419,7 +431,8 @@ def main():
                             for k, v in qm.items()}
             rows = support_rows(True)
             kbytes = toks * D * e
-            vbytes = rows * D * e
+            # softmax weights every selected token: all their value rows
+            vbytes = (toks if name == "softmax_topk" else rows) * D * e
             mbytes = meta_gauss_bytes if name == "gauss" else meta_bbox_bytes
             r.update(selected_pages=pages, selected_tokens=toks, support_v_rows=rows,
                      bytes={"metadata": mbytes, "tail_refresh": tail_bytes,
@@ -438,6 +451,8 @@ def main():
                 # hundred per head: left out)
                 "entmax_scores": kbytes + (0 if name == "gauss" else sel_positions * G * 4),
             }
+            if "softmax" in r["phase_ms"]:
+                r["kernel_bytes"]["softmax"] = kbytes + vbytes
             if "entmax_small" in r["phase_ms"]:
                 # keys of the selection and value rows of the support read,
                 # the output rows written
@@ -494,10 +509,21 @@ def main():
         if base in results and head_name in results:
             speedups["%s_over_%s" % (head_name, base)] = round(
                 results[base]["median_ms"] / head["median_ms"], 3)
-        for tk in ("topk", "topk_split"):
+        for tk in ("topk", "topk_split", "softmax_topk"):
             if base in results and tk in results:
                 speedups["%s_over_%s" % (tk, base)] = round(
                     results[base]["median_ms"] / results[tk]["median_ms"], 3)
+
+    if "topk" in results and "softmax_topk" in results:
+        speedups["topk_over_softmax_topk"] = round(
+            results["softmax_topk"]["median_ms"] / results["topk"]["median_ms"], 3)
+
+    extra = {}
+    names = [x for x in args.extra.split(",") if x]
+    if names:
+        del buf, kv
+        for name in names:
+            extra[name] = other_workload(name, args, flush, dev_ev, log)
 
     cpu, cpu_more = None, None
     n_cpu = B * H if args.cpu_units < 0 else args.cpu_units
@@ -532,8 +558,120 @@ def main():
         "hbm_read_probe_gbps": round(read_probe_gbps, 1),
         "legs": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                      for kk, vv in v.items()} for k, v in results.items()},
+        "workloads": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def fresh_queries(inp, gen):
+    """A new query set of the workload's recipe, drawn on the device in one
+    pass: for clustered keys each query head is the sum of 1-3 distinct
+    cluster means of its KV head over sqrt(count); else N(0, I)."""
+    import torch
+    spec = inp.spec
+    B, H, G, D = spec.batch, spec.num_kv_heads, spec.group, spec.head_dim
+    dev = inp.q.device
+    if inp.cluster_means is None:
+        return torch.randn(B, H * G, D, generator=gen, device=dev)
+    C = spec.n_clusters
+    cnt = torch.randint(1, 4, (B, H, G), generator=gen, device=dev)
+    order = torch.rand(B, H, G, C, generator=gen, device=dev).argsort(dim=-1)
+    pick = torch.zeros(B, H, G, C, device=dev)
+    pick.scatter_(-1, order[..., :3], (torch.arange(3, device=dev) < cnt[..., None]).float())
+    q = torch.matmul(pick, inp.cluster_means.contiguous()) / cnt[..., None].float().sqrt()
+    return q.reshape(B, H * G, D).contiguous()
+
+
+def other_workload(name, args, flush, dev_ev, log):
+    """The Gaussian decode step on another workload, timed per step with a
+    HIP event pair (the cache flush outside).  On a workload with spare
+    pages (ragged_pool_b16) every step first appends one token to every
+    sequence (key from the sequence's last cluster, value N(0, I), written
+    into the pool through the page table), and draws a fresh query set; the
+    tail-page metadata refresh runs inside the scoring launch.  The step
+    time includes the append; decode_ms is the part after it."""
+    import numpy as np
+    import torch
+
+    import sparse_entmax_attention_amd as ekv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    spec = workloads.workload(name)
+    log("[bench] generating %s seed %d" % (name, args.seed))
+    inp = workloads.generate(spec, args.seed, dev)
+    kv = ekv.PagedKV(inp.k, inp.v, inp.page_table, inp.seq_lens, spec.group)
+    buf = ekv.DecodeBuffers(kv, bbox=False)
+    buf.build_meta()
+    B, H, G, D, P = spec.batch, spec.num_kv_heads, spec.group, spec.head_dim, spec.page_size
+    alpha, delta = spec.alphas[0], spec.delta
+    n_steps = args.extra_warmup + args.extra_steps
+    appending = spec.spare_pages > 0
+    if appending and n_steps > spec.spare_pages * P:
+        raise SystemExit("%s: %d steps do not fit %d spare pages" % (name, n_steps, spec.spare_pages))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 1)
+    if appending:
+        dt = spec.torch_dtype
+        newk = (inp.cluster_means[None, :, :, -1, :] +
+                0.3 * torch.randn(n_steps, B, H, D, generator=gen, device=dev)).to(dt)
+        newv = torch.randn(n_steps, B, H, D, generator=gen, device=dev).to(dt)
+        qs = [fresh_queries(inp, gen) for _ in range(n_steps)]
+        bidx = torch.arange(B, device=dev)
+    else:
+        qs = [inp.q] * n_steps
+    torch.cuda.synchronize()
+
+    def append(s):
+        pos = inp.seq_lens.long()
+        slot = inp.page_table[bidx, pos // P].long()
+        off = pos % P
+        inp.k[slot, :, off, :] = newk[s]
+        inp.v[slot, :, off, :] = newv[s]
+        inp.seq_lens += 1
+
+    def decode(s):
+        buf.refresh_score(qs[s], ekv.EKV_SCORE_GAUSS)
+        buf.select_gauss(alpha, delta)
+        buf.entmax(qs[s], alpha, tau_hint=buf.tau_hat)
+
+    evs = [(dev_ev.new(), dev_ev.new(), dev_ev.new()) for _ in range(n_steps)]
+    for s in range(n_steps):
+        if flush is not None:
+            flush(s)
+        dev_ev.record(evs[s][0], stream)
+        if appending:
+            append(s)
+        dev_ev.record(evs[s][1], stream)
+        decode(s)
+        dev_ev.record(evs[s][2], stream)
+    torch.cuda.synchronize()
+    timed = evs[args.extra_warmup:]
+    step = [dev_ev.ms(a, c) for a, _, c in timed]
+    dec = [dev_ev.ms(b2, c) for _, b2, c in timed]
+    dev_ev.close()
+    med = statistics.median(step)
+    lens = inp.seq_lens.cpu().tolist()
+    n_pages = sum((L + P - 1) // P for L in lens)
+    cnt = buf.count.cpu().numpy()
+    meta = n_pages * H * 2 * D * 4
+    res = {"steps": args.extra_steps, "warmup": args.extra_warmup,
+           "median_ms": med, "p10_ms": float(np.percentile(step, 10)),
+           "p90_ms": float(np.percentile(step, 90)),
+           "decode_median_ms": statistics.median(dec),
+           "tokens_per_s": B / (med * 1e-3),
+           "config": {"batch": B, "kv_heads": H, "group": G, "head_dim": D,
+                      "page_size": P, "kv_dtype": spec.kv_dtype, "alpha": alpha,
+                      "delta": delta, "selector": "gauss",
+                      "seq_lens_after": lens,
+                      "append_per_step": appending},
+           "selected_pages_last_step": int(cnt.sum()),
+           "metadata_bytes": meta}
+    log("[bench] %s: median %.1f us per step (%s), %.0f tokens/s" % (
+        name, med * 1e3, "with the append" if appending else "Gaussian step",
+        res["tokens_per_s"]))
+    return {k: (round(v, 5) if isinstance(v, float) else v) for k, v in res.items()}
 
 
 def cpu_baseline(inp, spec, n_units, alpha, delta, log):
