@@ -571,9 +571,10 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
         }
         if (valid && li < G) gpage[row0 + static_cast<size_t>(li) * max_pages + lp] = mine;
       }
-      // refill: the step R further on, in this tile or the next
+      // refill: the step R further on, in this tile or the wave's next one
+      // (none after its last tile)
       if (s + R < NSTEP) issue(st, cur, slots_cur, s + R);
-      else issue(st, nxt, slots_next, s + R - NSTEP);
+      else if (more) issue(st, nxt, slots_next, s + R - NSTEP);
     }
 
     // tile summaries (every tile holds at least one valid page)
