@@ -18,6 +18,8 @@
 // HBM reads: selected K once, V only on the support, z twice.
 #include <float.h>
 
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace ekv {
@@ -680,96 +682,90 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   double blo = L, bhi = Md;  // bracket for the fallback
 
   // Exact solve by support iteration (r in {1, 2}, candidates staged), by
-  // wave 0 alone.  In y = z - M, t is kept a lower bound on tau (F(t) >= 1
-  // with F(t) = sum max(y - t, 0)^r); it starts at L - M.  Each pass sums,
-  // over S(t) = {y > t}, the count K, sum y and sum y^2, and finds min_S y.
-  // The closed form t* of tau for the support S (sparsemax: (sum y - 1)/K;
-  // 1.5-entmax: the smaller root of sum_S (y - t)^2 = 1) is tau itself when
-  // t* < min_S y, since then S(t*) = S.  Otherwise t moves up: for r = 1 to
-  // t* (over a superset of the support the terms below tau are negative, so
-  // t* <= tau: Michelot's iteration), for r = 2 by a Newton step on
-  // F^(1/2) - 1 (convex, so the step stays below tau).  Lanes sum their
-  // candidates segment by segment in a fixed order and the wave reduces in
-  // a fixed pattern, so the result is the same on every run.
+  // wave 0 alone, in y = z - M from t = L - M (a lower bound on tau - M):
+  // wave_support_iter over the candidates in registers (float32 sums, the
+  // final support's closed form in double), or, beyond 2048 candidates, the
+  // same iteration over LDS in double.  Lanes sum their candidates in a
+  // fixed order and the wave reduces in a fixed pattern, so the result is
+  // the same on every run.
   if (staged && (r == 1 || r == 2)) {
     if (wave == 0) {
-      // Up to R * kWave candidates are held in registers: candidate e (in
-      // segment order) goes to lane e % 64, slot e / 64.
-      // Segment starts in scalar registers (wave-uniform), so that locating
-      // a candidate is a compare chain rather than dependent LDS reads.
-      constexpr int R = 32;
+      // Up to 2048 candidates are held in registers: candidate e (in
+      // segment order) goes to lane e % 64, slot e / 64, as y = z - M; the
+      // slot count is the smallest power of two that holds them.  Segment
+      // starts in scalar registers (wave-uniform), so that locating a
+      // candidate is a compare chain rather than dependent LDS reads.
       int segs[NW + 1];
       segs[0] = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w)
         segs[w + 1] = segs[w] + __builtin_amdgcn_readfirstlane(s_ccnt[w]);
       const int n_all = segs[NW];
-      const bool in_regs = n_all <= R * kWave;
-      // register slots in use (uniform); the others are never visited
-      const int nslot = min(R, (n_all + kWave - 1) / kWave);
-      // (the loads are unconditional, from a clamped index, so that they
-      // are all in flight together)
-      float yr[R];
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const int e = lane + k * kWave;
-        int base = 0, w = 0;
-#pragma unroll
-        for (int v = 1; v < NW; ++v)
-          if (e >= segs[v]) { w = v; base = segs[v]; }
-        const bool on = in_regs && e < n_all;
-        const float zc = cand[on ? w * CSEG + (e - base) : 0];
-        yr[k] = on ? zc : -INFINITY;
-      }
-
-      double t = L - Md;
+      // the start, L - M rounded down to a float (a lower bound on tau - M)
+      float t0 = static_cast<float>(L - Md);
+      if (static_cast<double>(t0) > L - Md) t0 = nextafterf(t0, -INFINITY);
       double res = 0.0;
       bool ok = false;
-      for (int it = 0; it < kTauIters; ++it) {
-        int K = 0;
-        double SY = 0.0, SY2 = 0.0;
-        float zmin = FLT_MAX;
-        auto visit = [&](float zc) {  // branch-free
-          const double y = static_cast<double>(zc) - Md;
-          const bool in = y > t;
-          const double yy = in ? y : 0.0;
-          K += in ? 1 : 0;
-          SY += yy;
-          SY2 = fma(yy, yy, SY2);
-          zmin = in ? fminf(zmin, zc) : zmin;
-        };
-        if (in_regs) {
+      auto solve_in_regs = [&](auto slots) {
+        constexpr int RR = decltype(slots)::value;
+        float y[RR];
 #pragma unroll
-          for (int k = 0; k < R; ++k)
-            if (k < nslot) visit(yr[k]);
-        } else {
+        for (int k = 0; k < RR; ++k) {
+          const int e = lane + k * kWave;
+          int base = 0, w = 0;
+#pragma unroll
+          for (int v = 1; v < NW; ++v)
+            if (e >= segs[v]) { w = v; base = segs[v]; }
+          const bool on = e < n_all;
+          const float zc = cand[on ? w * CSEG + (e - base) : 0];
+          y[k] = on ? zc - M : -INFINITY;
+        }
+        ok = wave_support_iter<RR>(y, t0, r, kTauIters, res);
+      };
+      if (n_all <= 4 * kWave) solve_in_regs(std::integral_constant<int, 4>());
+      else if (n_all <= 8 * kWave) solve_in_regs(std::integral_constant<int, 8>());
+      else if (n_all <= 16 * kWave) solve_in_regs(std::integral_constant<int, 16>());
+      else if (n_all <= 32 * kWave) solve_in_regs(std::integral_constant<int, 32>());
+      else {
+        // more candidates than registers: the same iteration over LDS, in
+        // double
+        double t = static_cast<double>(t0);
+        for (int it = 0; it < kTauIters; ++it) {
+          int K = 0;
+          double SY = 0.0, SY2 = 0.0;
+          float zmin = FLT_MAX;
           for (int w = 0; w < NW; ++w)
-            for (int i = lane; i < s_ccnt[w]; i += kWave) visit(cand[w * CSEG + i]);
-        }
-        wave_reduce_pass(K, SY, SY2, zmin);
-        if (K == 0) break;
-        const double kd = static_cast<double>(K);
-        const double ymin = static_cast<double>(zmin) - Md;
-        double tn;
-        if (r == 1) {
-          tn = (SY - 1.0) / kd;
-          if (tn < ymin) { res = tn; ok = true; break; }
-        } else {
-          const double disc = SY * SY - kd * (SY2 - 1.0);
-          if (disc >= 0.0) {
-            const double ts = (SY - sqrt(disc)) / kd;
-            if (ts < ymin) { res = ts; ok = true; break; }
+            for (int i = lane; i < s_ccnt[w]; i += kWave) {
+              const float zc = cand[w * CSEG + i];
+              const double y = static_cast<double>(zc) - Md;
+              const bool in = y > t;
+              const double yy = in ? y : 0.0;
+              K += in ? 1 : 0;
+              SY += yy;
+              SY2 = fma(yy, yy, SY2);
+              zmin = in ? fminf(zmin, zc) : zmin;
+            }
+          wave_reduce_pass(K, SY, SY2, zmin);
+          if (K == 0) break;
+          const double kd = static_cast<double>(K);
+          const double ymin = static_cast<double>(zmin) - Md;
+          double tn;
+          if (r == 1) {
+            tn = (SY - 1.0) / kd;
+            if (tn < ymin) { res = tn; ok = true; break; }
+          } else {
+            const double disc = SY * SY - kd * (SY2 - 1.0);
+            if (disc >= 0.0) {
+              const double ts = (SY - sqrt(disc)) / kd;
+              if (ts < ymin) { res = ts; ok = true; break; }
+            }
+            const double F = SY2 - 2.0 * t * SY + kd * t * t;
+            const double Dv = SY - kd * t;
+            tn = t + (F - sqrt(F)) / Dv;
           }
-          const double F = SY2 - 2.0 * t * SY + kd * t * t;
-          const double Dv = SY - kd * t;
-          tn = t + (F - sqrt(F)) / Dv;
+          if (!(tn > t)) { res = t; ok = true; break; }
+          t = tn;
         }
-        if (!(tn > t)) {  // converged to rounding without a clean support
-          res = t;
-          ok = true;
-          break;
-        }
-        t = tn;
       }
       if (lane == 0) {
         s_wsolved = ok ? 1 : 0;

@@ -98,6 +98,91 @@ __device__ __forceinline__ float pow_r(float x, int r, float rg) {
   return x > 0.f ? powf(x, rg) : 0.f;
 }
 
+// Wave-wide sums of a, b, c and minimum of m, every value in every lane.
+// The four reductions are interleaved step by step (each swizzle of one
+// value covers the data hazard of the next), with the fixed pattern of the
+// single-value reductions: row swizzles, then the row broadcasts into lane 63.
+__device__ __forceinline__ void wave_sum3_min(float &a, float &b, float &c, float &m) {
+#define EKV_STEP(CTRL)                                  \
+  {                                                     \
+    const float a_ = dpp_f<CTRL>(a), b_ = dpp_f<CTRL>(b); \
+    const float c_ = dpp_f<CTRL>(c), m_ = dpp_f<CTRL>(m); \
+    a += a_; b += b_; c += c_; m = fminf(m, m_);         \
+  }
+  EKV_STEP(kDppRowMirror)
+  EKV_STEP(kDppRowHalfMirror)
+  EKV_STEP(kDppQuad2301)
+  EKV_STEP(kDppQuad1032)
+#undef EKV_STEP
+  const int big = __float_as_int(FLT_MAX);
+#define EKV_BCAST(CTRL, ROWS)                                                \
+  {                                                                          \
+    const float a_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(a), 0)); \
+    const float b_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(b), 0)); \
+    const float c_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(c), 0)); \
+    const float m_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(m), big)); \
+    a += a_; b += b_; c += c_; m = fminf(m, m_);                            \
+  }
+  EKV_BCAST(kDppRowBcast15, 0xA)
+  EKV_BCAST(kDppRowBcast31, 0xC)
+#undef EKV_BCAST
+  a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), kWave - 1));
+  b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), kWave - 1));
+  c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), kWave - 1));
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), kWave - 1));
+}
+
+// Exact threshold by support iteration, one wave, over R register slots of y
+// per lane (-inf marks an unused slot), from t0, a lower bound on tau in the
+// same origin: over S(t) = {y > t} the closed form t* of the threshold of
+// that support (sparsemax: (sum y - 1)/K; 1.5-entmax: the smaller root of
+// sum_S (y - t)^2 = 1) is tau once t* < min_S y, since then S(t*) = S;
+// otherwise t moves up, to t* for r = 1 (Michelot's step: over a superset of
+// the support the terms below tau are negative, so t* <= tau) and by a
+// Newton step on F^(1/2) - 1 for r = 2 (convex, so the step stays below
+// tau).  Sums are taken in float32 (each lane's R slots in order, then the
+// wave in a fixed pattern: the result is the same on every run), the steps
+// in float32, and the closed form of the final support in double.  No slot
+// is branched on.  Returns false when no support is found in `iters` passes.
+template <int R>
+__device__ __forceinline__ bool wave_support_iter(const float (&y)[R], float t0,
+                                                  int r, int iters, double &tau) {
+  float t = t0;
+  for (int it = 0; it < iters; ++it) {
+    float kf = 0.f, sy = 0.f, sy2 = 0.f, ymin = FLT_MAX;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const bool in = y[k] > t;
+      const float yy = in ? y[k] : 0.f;
+      kf += in ? 1.f : 0.f;
+      sy += yy;
+      sy2 = fmaf(yy, yy, sy2);
+      ymin = fminf(ymin, in ? y[k] : FLT_MAX);
+    }
+    wave_sum3_min(kf, sy, sy2, ymin);  // kf: exact count
+    if (kf == 0.f) return false;
+    const double kd = static_cast<double>(kf);
+    const double SY = static_cast<double>(sy), SY2 = static_cast<double>(sy2);
+    float tn;
+    if (r == 1) {
+      tn = (sy - 1.f) / kf;
+      if (tn < ymin) { tau = (SY - 1.0) / kd; return true; }
+    } else {
+      const float disc = sy * sy - kf * (sy2 - 1.f);
+      if (disc >= 0.f && (sy - sqrtf(disc)) / kf < ymin) {
+        tau = (SY - sqrt(fmax(SY * SY - kd * (SY2 - 1.0), 0.0))) / kd;
+        return true;
+      }
+      const float F = fmaf(kf * t, t, fmaf(-2.f * t, sy, sy2));
+      const float Dv = fmaf(-kf, t, sy);
+      tn = t + (F - sqrtf(F)) / Dv;
+    }
+    if (!(tn > t)) { tau = t; return true; }  // converged to rounding
+    t = tn;
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------------------
 // 1a. Scores on the matrix cores (bfloat16 keys).
 //

@@ -20,51 +20,11 @@ constexpr int kSmallThreads = 512;
 constexpr int kSmallWaves = kSmallThreads / kWave;
 constexpr int kSmallIters = 64;  // support iterations before bisection
 
-// Wave-wide sums of a, b, c and minimum of m, every value in every lane.
-// The four reductions are interleaved step by step (each swizzle of one
-// value covers the data hazard of the next), with the fixed pattern of the
-// single-value reductions: row swizzles, then the row broadcasts into lane 63.
-__device__ __forceinline__ void wave_sum3_min(float &a, float &b, float &c, float &m) {
-#define EKV_STEP(CTRL)                                  \
-  {                                                     \
-    const float a_ = dpp_f<CTRL>(a), b_ = dpp_f<CTRL>(b); \
-    const float c_ = dpp_f<CTRL>(c), m_ = dpp_f<CTRL>(m); \
-    a += a_; b += b_; c += c_; m = fminf(m, m_);         \
-  }
-  EKV_STEP(kDppRowMirror)
-  EKV_STEP(kDppRowHalfMirror)
-  EKV_STEP(kDppQuad2301)
-  EKV_STEP(kDppQuad1032)
-#undef EKV_STEP
-  const int big = __float_as_int(FLT_MAX);
-#define EKV_BCAST(CTRL, ROWS)                                                \
-  {                                                                          \
-    const float a_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(a), 0)); \
-    const float b_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(b), 0)); \
-    const float c_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(c), 0)); \
-    const float m_ = __int_as_float(dpp_rows<CTRL, ROWS>(__float_as_int(m), big)); \
-    a += a_; b += b_; c += c_; m = fminf(m, m_);                            \
-  }
-  EKV_BCAST(kDppRowBcast15, 0xA)
-  EKV_BCAST(kDppRowBcast31, 0xC)
-#undef EKV_BCAST
-  a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), kWave - 1));
-  b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), kWave - 1));
-  c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), kWave - 1));
-  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), kWave - 1));
-}
-
 // One wave's exact threshold of n values y (ys[i] - shift; -inf past n) that
 // lie in [-1, 0] or below, with max y = 0, returned in the same offset.
-// r in {1, 2}: support iteration from t = -1: the closed form t* of the
-// threshold of the support S(t) = {y > t} (sparsemax: (sum y - 1)/K;
-// 1.5-entmax: the smaller root of sum_S (y - t)^2 = 1) is tau once t* <
-// min_S y; otherwise t moves up (Michelot's step for r = 1, a Newton step on
-// F^(1/2) for r = 2; both stay below tau).  Other r, or no clean support
-// after kSmallIters passes: bisection on [-1, 0].  Sums are taken in float32
-// (each lane's R slots in order, then the wave in a fixed pattern), the
-// steps in float32, and the closed form of the final support in double.  No
-// slot is branched on: a slot past n holds -inf and drops out of every sum.
+// r in {1, 2}: the support iteration from t = -1 (tau >= max y - 1).  Other
+// r, or no clean support after kSmallIters passes: bisection on [-1, 0]
+// (sums in float32 per lane, the wave in a fixed pattern).
 template <int R>
 __device__ __forceinline__ double wave_solve(const float *ys, int n, float shift,
                                              int r, float rg) {
@@ -77,37 +37,8 @@ __device__ __forceinline__ double wave_solve(const float *ys, int n, float shift
     y[k] = i < n ? y[k] : -INFINITY;
   }
   if (r == 1 || r == 2) {
-    float t = -1.f;
-    for (int it = 0; it < kSmallIters; ++it) {
-      float kf = 0.f, sy = 0.f, sy2 = 0.f, ymin = FLT_MAX;
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const bool in = y[k] > t;
-        const float yy = in ? y[k] : 0.f;
-        kf += in ? 1.f : 0.f;
-        sy += yy;
-        sy2 = fmaf(yy, yy, sy2);
-        ymin = fminf(ymin, in ? y[k] : FLT_MAX);
-      }
-      wave_sum3_min(kf, sy, sy2, ymin);  // kf: exact count
-      if (kf == 0.f) break;
-      const double kd = static_cast<double>(kf);
-      const double SY = static_cast<double>(sy), SY2 = static_cast<double>(sy2);
-      float tn;
-      if (r == 1) {
-        tn = (sy - 1.f) / kf;
-        if (tn < ymin) return (SY - 1.0) / kd;
-      } else {
-        const float disc = sy * sy - kf * (sy2 - 1.f);
-        if (disc >= 0.f && (sy - sqrtf(disc)) / kf < ymin)
-          return (SY - sqrt(fmax(SY * SY - kd * (SY2 - 1.0), 0.0))) / kd;
-        const float F = fmaf(kf * t, t, fmaf(-2.f * t, sy, sy2));
-        const float Dv = fmaf(-kf, t, sy);
-        tn = t + (F - sqrtf(F)) / Dv;
-      }
-      if (!(tn > t)) return t;  // converged to rounding
-      t = tn;
-    }
+    double tau;
+    if (wave_support_iter<R>(y, -1.f, r, kSmallIters, tau)) return tau;
   }
   // bisection: sum max(y - mid, 0)^r >= 1 keeps mid below tau
   double lo = -1.0, hi = 0.0;
