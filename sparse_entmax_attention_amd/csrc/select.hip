@@ -317,12 +317,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_topk(
 // Lists or page data beyond the LDS capacities are read from global memory
 // instead (same arithmetic, slower).
 // ---------------------------------------------------------------------------
-constexpr int kGtThreads = 512;
+constexpr int kGtThreads = 1024;
 constexpr int kGtWaves = kGtThreads / kWave;
 constexpr int kGtSvItems = 128;   // survivor tiles whose (m, s) sit in LDS
 constexpr int kGtKzItems = 128;   // keep-candidate tiles whose zhat sit in LDS
 constexpr int kGtListCap = 4096;  // entries of each tile list
 constexpr float kPruneSigmas = 8.5f;
+constexpr float kGtDrop = 1e-12f;  // page terms dropped from later passes
 
 // Standard normal tail pieces at c: Phi(c) and the density phi(c).
 // For a = |c|, the upper tail Q(a) = phi(a) R(a) with R the Mills ratio,
@@ -648,8 +649,16 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     const bool last = e.y < 0.f;
     const float sd = last ? -1.0f - e.y : e.y;
     const float nn = last ? last_n : static_cast<float>(P);
-    if constexpr (RULE) gauss_term_rule(e.x, sd, nn, t, rule, f, df);
-    else gauss_term(e.x, sd, nn, t, r, f, df);
+    float tf = 0.f, tdf = 0.f;
+    if constexpr (RULE) gauss_term_rule(e.x, sd, nn, t, rule, tf, tdf);
+    else gauss_term(e.x, sd, nn, t, r, tf, tdf);
+    f += tf;
+    df += tdf;
+    // A page's term only falls as tau rises (every step is upward): once
+    // below kGtDrop it is dropped for the remaining passes.  Together the
+    // dropped terms stay under 16384 kGtDrop, far below float rounding of
+    // F ~ 1.
+    if (i < kGtSvItems && tf < kGtDrop) s_sv[i * kPageTile + lane].x = -INFINITY;
   };
   float tau = tau_lo, prev_step = INFINITY;
   for (int it = 0; it < 64; ++it) {
