@@ -333,7 +333,8 @@ constexpr float kGtDrop = 1e-12f;  // page terms dropped from later passes
 // evaluated here in float32.  Its large-x behaviour is R ~ 1/x, as it should
 // be, and phi(a) underflows to 0 past a ~ 13.2.  Because Q is a product,
 // its relative accuracy holds far into the tail; Phi(c) = Q(-c) for c < 0
-// and 1 - Q(c) otherwise.
+// and 1 - Q(c) otherwise.  fit_mills.py (beside this file) refits such a
+// rational function and checks these constants.
 __device__ __forceinline__ void norm_cdf_pdf(float c, float &Phi, float &phi) {
   const float a = fabsf(c);
   phi = 0.39894228040143268f *
