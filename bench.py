@@ -107,8 +107,8 @@ def kernel_source_hash():
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled), or None when there is none or the
-    kernel's sources changed since it was taken."""
+    (L2-to-memory read and write requests counted by size), or None when
+    there is none or the kernel's sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
