@@ -517,6 +517,19 @@ def main():
     if "topk" in results and "softmax_topk" in results:
         speedups["topk_over_softmax_topk"] = round(
             results["softmax_topk"]["median_ms"] / results["topk"]["median_ms"], 3)
+    # The same speedups against full-cache baselines that would stream their
+    # bytes at the measured read ceiling (the 2 GiB read probe): the bytes
+    # each baseline must read, divided by the probe's rate.  A baseline
+    # kernel cannot beat this, so these ratios bound the speedup from below.
+    floor_ms = {}
+    for base in ("softmax_full", "entmax_full"):
+        if base in results:
+            floor_ms[base] = results[base]["step_bytes"] / (read_probe_gbps * 1e9) * 1e3
+    for base, fms in floor_ms.items():
+        for leg in (head_name, "topk"):
+            if leg in results:
+                speedups["%s_over_%s_at_read_probe_rate" % (leg, base)] = round(
+                    fms / results[leg]["median_ms"], 3)
 
     extra = {}
     names = [x for x in args.extra.split(",") if x]
@@ -556,6 +569,7 @@ def main():
         "speedups": speedups,
         "meta_build_ms": round(meta_build_ms, 4),
         "hbm_read_probe_gbps": round(read_probe_gbps, 1),
+        "baseline_floor_ms_at_read_probe_rate": {k: round(v, 4) for k, v in floor_ms.items()},
         "legs": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                      for kk, vv in v.items()} for k, v in results.items()},
         "workloads": extra,
