@@ -207,26 +207,47 @@ __device__ __forceinline__ float bf16_part(float x, int part) {
   return part == 0 ? p0 : part == 1 ? p1 : p2;
 }
 
+// A of the MFMA for the G query heads of KV head h in sequence b: row
+// 4 part + e of pass ps is the part-th bfloat16 part of zscale q_{4 ps + e}
+// (rows 12..15 and heads past G are zero), lane n + 16 kb holding
+// coordinates 32 s + 8 kb .. + 7 of its row for each k-step s.  Every load
+// is issued before any is used (rows with no head read head 0 and are zeroed
+// afterwards): a load behind a branch would be waited for on its own, one
+// memory round trip after another.  q is 16-byte aligned (the entry points
+// check it) and D a multiple of 32.
 template <int D, int G>
 __device__ __forceinline__ void load_q_parts(bf16x8_t (&a)[(G + 3) / 4][D / 32],
                                              const float *q, int b, int h,
                                              int H, float zscale) {
+  constexpr int NP = (G + 3) / 4, KS = D / 32;
   const int lane = threadIdx.x & (kWave - 1);
   const int n = lane & 15, kb = lane >> 4;
   const int Hq = H * G;
+  float4 raw[NP][KS][2];
 #pragma unroll
-  for (int ps = 0; ps < (G + 3) / 4; ++ps) {
+  for (int ps = 0; ps < NP; ++ps) {
+    const int g = (n & 3) + 4 * ps;
+    const float *src = q + (static_cast<size_t>(b) * Hq + h * G + (g < G ? g : 0)) * D +
+                       8 * kb;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      raw[ps][s][0] = *reinterpret_cast<const float4 *>(src + 32 * s);
+      raw[ps][s][1] = *reinterpret_cast<const float4 *>(src + 32 * s + 4);
+    }
+  }
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
     const int part = n >> 2, g = (n & 3) + 4 * ps;
+    const bool on = part < 3 && g < G;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s)
+    for (int s = 0; s < KS; ++s) {
+      const float x[8] = {raw[ps][s][0].x, raw[ps][s][0].y, raw[ps][s][0].z,
+                          raw[ps][s][0].w, raw[ps][s][1].x, raw[ps][s][1].y,
+                          raw[ps][s][1].z, raw[ps][s][1].w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = 0.f;
-        if (part < 3 && g < G)
-          x = bf16_part(q[(static_cast<size_t>(b) * Hq + h * G + g) * D +
-                          32 * s + 8 * kb + i] * zscale, part);
-        a[ps][s][i] = static_cast<__bf16>(x);
-      }
+      for (int i = 0; i < 8; ++i)
+        a[ps][s][i] = static_cast<__bf16>(on ? bf16_part(x[i] * zscale, part) : 0.f);
+    }
   }
 }
 

@@ -75,22 +75,40 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   static_assert(kKRing % NT16 == 0, "a body holds whole pages");
   __shared__ int pref[kMaxUnits + 1];
   __shared__ int tmp[kDecWaves];
+  // Per wave: the current page's kept scores (G rows of P), and the page
+  // maxima and candidate masks of the chunk's pages (G rows of 64).  The
+  // scores leave in one 16-byte store per lane per page and the page
+  // records once per chunk: stores cost the key stream more by their
+  // number than by their bytes.
+  constexpr int ZS = G * P < 256 ? 256 : G * P;
+  __shared__ __align__(16) float s_z[kDecWaves][ZS];
+  __shared__ float s_pm[kDecWaves][G][kWave];
+  __shared__ unsigned long long s_mk[kDecWaves][G][kWave];
   const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
                                                    count, units, H, P, 1);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, kb = lane >> 4;
   const int nwaves = gridDim.x * kDecWaves;
+  float *zst = s_z[wave];
   const int wg = blockIdx.x * kDecWaves + wave;
   const int per = ((total + U - 1) / U + nwaves - 1) / nwaves;  // bodies
   const int f0 = wg * per * U;
   const int f1 = min(total, f0 + per * U);
   if (f0 >= f1) return;  // whole waves; no block barrier follows
 
+  // Keys of 16-token group t of page (slot, h) through a buffer resource on
+  // the page: the page's address stays in scalar registers and every load
+  // of the stream shares one per-lane offset register.
+  const int key_off = 2 * (n * D + 8 * kb);
   auto issue = [&](bf16x8_t (&bv)[KS], int slot, int h, int t) {
-    const uint16_t *row = kpool + pool_row(slot, h, 16 * t + n, H, P, D) + 8 * kb;
+    const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(kpool + pool_row(slot, h, 0, H, P, D)),
+        static_cast<short>(0), 2 * P * D, 0x00020000);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      bv[s] = *reinterpret_cast<const bf16x8_t *>(row + 32 * s);
+      bv[s] = __builtin_bit_cast(
+          bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(pr, key_off + 64 * s,
+                                                          32 * D * t, 0));
   };
   auto lane_val = [](int x, int i) { return __builtin_amdgcn_readlane(x, i); };
 
@@ -99,47 +117,50 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   float flo[NPASS];                 // score floor of this lane's head 4 ps + kb
   int run[NPASS];                   // candidates so far in the page, per head
   unsigned long long pbits[NPASS];  // the page's candidate mask, per head
-  int cur_u = -1;
-  for (int c0 = f0; c0 < f1; c0 += kWave) {
-    const int nc = min(kWave, f1 - c0);        // pages in this chunk
+  for (int c0 = f0; c0 < f1;) {
+    // A chunk is up to 64 pages of one unit, so the unit's query parts and
+    // score floors are loaded here, while no keys are in flight: loading
+    // them inside the stream would hold their float32 sources in registers
+    // beside the ring, and the extra registers cost a wave per SIMD.
+    const int u = __builtin_amdgcn_readfirstlane(find_unit(pref, units, c0));
+    const int c1 = min(min(c0 + kWave, f1), pref[u + 1]);
+    const int nc = c1 - c0;                    // pages in this chunk
     const int nbc = (nc + U - 1) / U;          // bodies in this chunk
+    const int h = u % H, b = u / H;
+    load_q_parts<D, G>(a, q, b, h, H, zscale);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int g = 4 * ps + kb;
+      flo[ps] = g < G ? hint_floor(tau_hint, u * G + g) : -INFINITY;
+    }
     // page references, one page per lane (lanes past the chunk repeat its last)
-    const int f = c0 + min(lane, nc - 1);
-    const int ru = find_unit(pref, units, f);
-    const int rj = f - pref[ru];
-    const int rb = ru / H;
+    const int rj = c0 + min(lane, nc - 1) - pref[u];
     int rlp;
-    if constexpr (SEL) rlp = sel[static_cast<size_t>(ru) * max_pages + rj];
+    if constexpr (SEL) rlp = sel[static_cast<size_t>(u) * max_pages + rj];
     else rlp = rj;
-    const int rnt = page_tokens(rlp, seq_lens[rb], P);
-    const int rslot = page_table[static_cast<size_t>(rb) * max_pages + rlp];
+    const int rnt = page_tokens(rlp, seq_lens[b], P);
+    const int rslot = page_table[static_cast<size_t>(b) * max_pages + rlp];
     auto body_page = [&](int k, int t) { return min(k * U + t, nc - 1); };
 #pragma unroll
     for (int s = 0; s < kKRing; ++s) {
-      const int i = body_page(0, s / NT16);
-      issue(ring[s], lane_val(rslot, i), lane_val(ru, i) % H, s % NT16);
+      __builtin_amdgcn_sched_barrier(0);  // issued in the order they are used
+      issue(ring[s], lane_val(rslot, body_page(0, s / NT16)), h, s % NT16);
     }
     for (int k = 0; k < nbc; ++k) {
       float pm[NPASS][4];
 #pragma unroll
       for (int s = 0; s < kKRing; ++s) {
+        // Groups stay in program order: the compiler's scheduler would
+        // otherwise gather the refills at the end of the body, and the wait
+        // for the first group would then cover the whole body, leaving no
+        // keys in flight while the body is scored.
+        __builtin_amdgcn_sched_barrier(0);
         const int t = s / NT16, tt = s % NT16;
         const int i = k * U + t;               // page of the chunk
         const bool live = i < nc;
         const int ic = min(i, nc - 1);
-        const int u = lane_val(ru, ic);
         const int j = lane_val(rj, ic);
-        const int h = u % H;
         if (tt == 0) {
-          if (u != cur_u) {  // rare: the run enters another unit
-            cur_u = u;
-            load_q_parts<D, G>(a, q, u / H, h, H, zscale);
-#pragma unroll
-            for (int ps = 0; ps < NPASS; ++ps) {
-              const int g = 4 * ps + kb;
-              flo[ps] = g < G ? hint_floor(tau_hint, u * G + g) : -INFINITY;
-            }
-          }
 #pragma unroll
           for (int ps = 0; ps < NPASS; ++ps) {
             run[ps] = 0;
@@ -149,9 +170,6 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           }
         }
         const bool valid = 16 * tt + n < lane_val(rnt, ic);
-        const __amdgpu_buffer_rsrc_t zr = store_rsrc(
-            zbuf + static_cast<size_t>(u) * G * cap,
-            static_cast<size_t>(G) * cap * sizeof(float));
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
           f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -181,14 +199,12 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           const unsigned gb = static_cast<unsigned>(ball >> (16 * kb)) & 0xffffu;
           const int rank = run[ps] + __popc(gb & ((1u << n) - 1u));
           const bool keep = cand || (!valid && flo[ps] == -INFINITY);
-          store_if(zr, 4 * (g * cap + j * P + (cand ? rank : 16 * tt + n)),
-                   keep && g < G && live, valid ? zmine : -INFINITY);
+          if (keep && g < G) zst[g * P + (cand ? rank : 16 * tt + n)] = valid ? zmine : -INFINITY;
           run[ps] += __popc(gb);
           pbits[ps] |= static_cast<unsigned long long>(gb) << (16 * tt);
         }
         if (tt == NT16 - 1) {
-          // the page's maxima, lane g holding head g's
-          float mine = 0.f;
+          // the page's maxima and candidate masks, kept for the chunk's end
 #pragma unroll
           for (int ps = 0; ps < NPASS; ++ps)
 #pragma unroll
@@ -196,38 +212,79 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
               const int g = 4 * ps + e;
               if (g < G) {
                 const float m = group_max<16>(pm[ps][e]);
-                const float m0 = __shfl(m, 0, kWave);
-                mine = lane == g ? m0 : mine;
+                if (lane == 0) s_pm[wave][g][i] = m;
               }
             }
-          const int ps_ = pm_stride(max_pages);
-          const __amdgpu_buffer_rsrc_t pr = store_rsrc(
-              pmax + static_cast<size_t>(u) * G * ps_,
-              static_cast<size_t>(G) * ps_ * sizeof(float));
-          store_if(pr, 4 * (lane * ps_ + j), lane < G && live, mine);
-          // candidate masks: lane 16 e of pass ps writes head 4 ps + e's
-          const __amdgpu_buffer_rsrc_t mr = store_rsrc(
-              pmask + static_cast<size_t>(u) * G * ps_,
-              static_cast<size_t>(G) * ps_ * sizeof(unsigned long long));
 #pragma unroll
           for (int ps = 0; ps < NPASS; ++ps) {
-            typedef unsigned v2u __attribute__((ext_vector_type(2)));
             const int g = 4 * ps + kb;
-            const v2u w = {static_cast<unsigned>(pbits[ps]),
-                           static_cast<unsigned>(pbits[ps] >> 32)};
-            __builtin_amdgcn_raw_buffer_store_b64(
-                w, mr, (n == 0 && g < G && live) ? 8 * (g * ps_ + j) : kDropOffset, 0, 0);
+            if (n == 0 && g < G) s_mk[wave][g][i] = pbits[ps];
           }
-          const __amdgpu_buffer_rsrc_t sr = store_rsrc(
-              slots + static_cast<size_t>(u) * max_pages,
-              static_cast<size_t>(max_pages) * sizeof(int32_t));
-          store_if(sr, 4 * j, lane == 0 && live, lane_val(rslot, ic));
+          // The page's kept scores: lane l writes floats 4 l .. 4 l + 3 of
+          // the G rows of P (of row 4 l / P), those of a row up to its count
+          // of kept scores rounded up to 4 (the rest of the page's range is
+          // never read) or, without a hint, the whole row.
+          int lim[NPASS];
+#pragma unroll
+          for (int ps = 0; ps < NPASS; ++ps) lim[ps] = flo[ps] == -INFINITY ? P : run[ps];
+          const __amdgpu_buffer_rsrc_t zr = store_rsrc(
+              zbuf + static_cast<size_t>(u) * G * cap,
+              static_cast<size_t>(G) * cap * sizeof(float));
+#pragma unroll
+          for (int k2 = 0; k2 < (G * P + 255) / 256; ++k2) {
+            const int f = 256 * k2 + 4 * lane;
+            const int g2 = f / P, pos = f - g2 * P;
+            int lg;
+            if constexpr (P == 64) {
+              lg = lim[k2 < NPASS ? k2 : 0];  // row 4 k2 + kb: this lane's own
+            } else {
+              // both shuffles on every lane (a lane that reads from an
+              // inactive one gets 0), then the pass of this lane's row
+              const int src = 16 * (g2 & 3);
+              const int l0 = __shfl(lim[0], src, kWave);
+              const int l1 = __shfl(lim[NPASS - 1], src, kWave);
+              lg = g2 >= 4 ? l1 : l0;
+            }
+            // read as floats, the type the rows were written with, so that
+            // the read stays ordered after those writes
+            const float *zf = zst + min(f, ZS - 4);
+            const f32x4_t v = {zf[0], zf[1], zf[2], zf[3]};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, zr,
+                (live && g2 < G && pos < lg) ? 4 * (g2 * cap + j * P + pos) : kDropOffset,
+                0, 0);
+          }
         }
         // refill: the same group of the next body
-        const int inx = body_page(k + 1, t);
-        issue(ring[s], lane_val(rslot, inx), lane_val(ru, inx) % H, tt);
+        issue(ring[s], lane_val(rslot, body_page(k + 1, t)), h, tt);
       }
     }
+    // the chunk's page records: lane l holds page l of the chunk
+    {
+      const int j0 = c0 - pref[u];
+      const bool on = lane < nc;
+      const int ps_ = pm_stride(max_pages);
+      const __amdgpu_buffer_rsrc_t sr = store_rsrc(
+          slots + static_cast<size_t>(u) * max_pages,
+          static_cast<size_t>(max_pages) * sizeof(int32_t));
+      store_if(sr, 4 * (j0 + lane), on, rslot);
+      const __amdgpu_buffer_rsrc_t pr = store_rsrc(
+          pmax + static_cast<size_t>(u) * G * ps_,
+          static_cast<size_t>(G) * ps_ * sizeof(float));
+      const __amdgpu_buffer_rsrc_t mr = store_rsrc(
+          pmask + static_cast<size_t>(u) * G * ps_,
+          static_cast<size_t>(G) * ps_ * sizeof(unsigned long long));
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        store_if(pr, 4 * (g * ps_ + j0 + lane), on, s_pm[wave][g][lane]);
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const unsigned long long mk = s_mk[wave][g][lane];
+        const v2u w = {static_cast<unsigned>(mk), static_cast<unsigned>(mk >> 32)};
+        __builtin_amdgcn_raw_buffer_store_b64(
+            w, mr, on ? 8 * (g * ps_ + j0 + lane) : kDropOffset, 0, 0);
+      }
+    }
+    c0 = c1;
   }
 }
 
