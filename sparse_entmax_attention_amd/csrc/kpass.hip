@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
       issue(ring[s], lane_val(rslot, body_page(0, s / NT16)), h, s % NT16);
     }
     for (int k = 0; k < nbc; ++k) {
-      float pm[NPASS][4];
+      float pm[NPASS];  // the page's maximum so far of this lane's head 4 ps + kb
 #pragma unroll
       for (int s = 0; s < kKRing; ++s) {
         // Groups stay in program order: the compiler's scheduler would
@@ -165,8 +165,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           for (int ps = 0; ps < NPASS; ++ps) {
             run[ps] = 0;
             pbits[ps] = 0ull;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pm[ps][e] = -FLT_MAX;
+            pm[ps] = -FLT_MAX;
           }
         }
         const bool valid = 16 * tt + n < lane_val(rnt, ic);
@@ -187,13 +186,13 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
           for (int e = 0; e < 4; ++e) {
             const float s1 = c[e] + __shfl_xor(c[e], 16, kWave);
             const float z = s1 + __shfl_xor(s1, 32, kWave);
-            if (valid) pm[ps][e] = fmaxf(pm[ps][e], z);
             zmine = kb == e ? z : zmine;
           }
           // Candidates (z above the head's floor) go to the next free entry
           // of the page's range; without a hint every valid token is one, at
           // its own position, and the invalid tail keeps -inf as before.
           const int g = 4 * ps + kb;
+          if (valid) pm[ps] = fmaxf(pm[ps], zmine);
           const bool cand = valid && zmine > flo[ps];
           const unsigned long long ball = __ballot(cand);
           const unsigned gb = static_cast<unsigned>(ball >> (16 * kb)) & 0xffffu;
@@ -206,15 +205,10 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
         if (tt == NT16 - 1) {
           // the page's maxima and candidate masks, kept for the chunk's end
 #pragma unroll
-          for (int ps = 0; ps < NPASS; ++ps)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int g = 4 * ps + e;
-              if (g < G) {
-                const float m = group_max<16>(pm[ps][e]);
-                if (lane == 0) s_pm[wave][g][i] = m;
-              }
-            }
+          for (int ps = 0; ps < NPASS; ++ps) {
+            const float m = group_max<16>(pm[ps]);  // head 4 ps + kb's, in every lane of the group
+            if (n == 0 && 4 * ps + kb < G) s_pm[wave][4 * ps + kb][i] = m;
+          }
 #pragma unroll
           for (int ps = 0; ps < NPASS; ++ps) {
             const int g = 4 * ps + kb;
