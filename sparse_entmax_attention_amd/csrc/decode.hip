@@ -51,11 +51,15 @@ SoftmaxWs softmax_ws_layout(const ekv_paged_kv &kv) {
   const size_t G = kv.group, D = kv.head_dim;
   const size_t mc = max_chunks(kv);
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  // partial slots: one per chunk (float32 K/V) or per streaming segment
+  // (bfloat16 K/V), whichever is more
+  const size_t slots = std::max(units * mc, softmax_stream_slots(kv));
   SoftmaxWs w;
   w.part_m = 0;
-  w.part_l = al(units * mc * G * 4);
-  w.part_o = al(w.part_l + units * mc * G * 4);
-  w.total = al(w.part_o + units * mc * G * D * 4);
+  w.part_l = al(slots * G * 4);
+  w.part_o = al(w.part_l + slots * G * 4);
+  w.seg = al(w.part_o + slots * G * D * 4);
+  w.total = al(w.seg + units * 2 * 4);
   return w;
 }
 
@@ -1360,10 +1364,11 @@ __global__ void k_fill_probs(const int32_t *__restrict__ seq_lens, int Hq,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K softmax.  Persistent blocks over chunks: scores into LDS (matrix
-// cores for bfloat16 keys), the chunk maximum m, the weights exp(s - m)
-// once per (token, head), then the weighted value sum on the vector units.
-// The chunk partials (m, l, acc) are merged in log-sum-exp form.
+// Split-K softmax over float32 K/V (bfloat16 K/V stream through softmax.hip).
+// Persistent blocks over chunks: scores into LDS, the chunk maximum m, the
+// weights exp(s - m) once per (token, head), then the weighted value sum on
+// the vector units.  The chunk partials (m, l, acc) are merged in
+// log-sum-exp form.
 // ---------------------------------------------------------------------------
 template <class E, int D, int G>
 __device__ __forceinline__ void chunk_scores_valu(
@@ -1398,59 +1403,6 @@ __device__ __forceinline__ void chunk_scores_valu(
       for (int j = 0; j < 8; ++j) a = fmaf(qs[g][j], x[j], a);
       a = group_sum<LPT>(a);
       if (li == g) s_sc[g][i] = valid ? a : -INFINITY;
-    }
-  }
-}
-
-template <int D, int G>
-__device__ __forceinline__ void chunk_scores_mfma(
-    const ChunkPages &cp, const uint16_t *kpool, const float *q, int b, int h,
-    int H, int P, int npos, float scale, float (*s_sc)[kChunkTokens]) {
-  constexpr int KS = D / 32;
-  constexpr int NPASS = (G + 3) / 4;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int n = lane & 15, kb = lane >> 4;
-  bf16x8_t a[NPASS][KS];
-  load_q_parts<D, G>(a, q, b, h, H, scale);
-  // Each wave takes 16-token groups wave, wave+4, ...; 4 groups in flight.
-  constexpr int NGR = kChunkTokens / 16;
-  constexpr int INF = 4;
-  for (int gr0 = wave; gr0 < NGR; gr0 += INF * kDecWaves) {
-    bf16x8_t bv[INF][KS];
-#pragma unroll
-    for (int k = 0; k < INF; ++k) {
-      const int i = 16 * (gr0 + k * kDecWaves) + n;
-      const int jj = i / P, t = i - jj * P;
-      const bool inb = i < npos;
-      const int slot = cp.slot[inb ? jj : 0];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (inb)
-          bv[k][s] = *reinterpret_cast<const bf16x8_t *>(
-              kpool + pool_row(slot, h, t, H, P, D) + 32 * s + 8 * kb);
-        else
-          bv[k][s] = bf16x8_t{};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < INF; ++k) {
-      const int i = 16 * (gr0 + k * kDecWaves) + n;
-      const int jj = i / P, t = i - jj * P;
-      const bool valid = i < npos && t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-#pragma unroll
-      for (int ps = 0; ps < NPASS; ++ps) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], bv[k][s], c, 0, 0, 0);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float p1 = __shfl_down(c[ii], 16, kWave);
-          const float p2 = __shfl_down(c[ii], 32, kWave);
-          const int g = 4 * ps + ii;
-          if (g < G && lane < 16) s_sc[g][i] = valid ? c[ii] + (p1 + p2) : -INFINITY;
-        }
-      }
     }
   }
 }
@@ -1518,11 +1470,7 @@ __global__ __launch_bounds__(kDecThreads) void k_softmax_partial(
                                 max_pages);
     lds_barrier();
     const int npos = npg * P;
-    if constexpr (sizeof(typename E::T) == 2)
-      chunk_scores_mfma<D, G>(cp, reinterpret_cast<const uint16_t *>(kpool), q,
-                              b, h, H, P, npos, scale, s_sc);
-    else
-      chunk_scores_valu<E, D, G>(cp, kpool, q, b, h, H, P, npos, scale, s_sc);
+    chunk_scores_valu<E, D, G>(cp, kpool, q, b, h, H, P, npos, scale, s_sc);
     lds_barrier();
     // chunk maximum per head, then the weights and their sum
     float m[G];
@@ -1616,190 +1564,6 @@ __global__ __launch_bounds__(kDecThreads) void k_softmax_partial(
       for (int ww = 1; ww < kDecWaves; ++ww) v += red[ww][threadIdx.x];
       part_l[pc * G + threadIdx.x] = v;
       part_m[pc * G + threadIdx.x] = m[threadIdx.x];
-    }
-    lds_barrier();
-  }
-}
-
-// Split-K softmax on the matrix cores (bfloat16 K/V).  Within a chunk every
-// wave runs its own online softmax over 16-token groups: scores of a group
-// from one MFMA pass, the group maximum m', the running state rescaled by
-// exp(m - m'), weights exp(s - m') broadcast to the lanes that hold the
-// group's value rows.  The K and V rows of two groups are in flight at once
-// and waves never wait for each other until the chunk's four states are
-// merged.
-template <int D, int G>
-__global__ __launch_bounds__(kDecThreads) void k_softmax_partial_mfma(
-    const uint16_t *__restrict__ kpool, const uint16_t *__restrict__ vpool,
-    const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
-    const int32_t *__restrict__ count, const float *__restrict__ q,
-    float scale, int units, int H, int P, int max_pages, int maxch,
-    float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_o) {
-  constexpr int KS = D / 32;
-  constexpr int NPASS = (G + 3) / 4;
-  constexpr int LPT = D / 8;      // lanes per value row
-  constexpr int TPI = kWave / LPT;  // value rows per load instruction
-  constexpr int NVI = 16 / TPI;   // value load instructions per 16 tokens
-  constexpr int NGR = kChunkTokens / 16;
-  __shared__ int pref[kMaxUnits + 1];
-  __shared__ int tmp[kDecWaves];
-  __shared__ ChunkPages cp;
-  __shared__ float s_m[kDecWaves][G];
-  __shared__ float s_l[kDecWaves][G];
-  __shared__ float s_acc[kDecWaves][G][D];
-  const int ppc = kChunkTokens / P;
-  const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
-                                                   count, units, H, P, ppc);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int n = lane & 15;
-  const int li = lane % LPT, sub = lane / LPT, d0 = li * 8;
-  bf16x8_t a[NPASS][KS];
-  int cur_u = -1;
-
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int u = find_unit(pref, units, w);
-    const int c = w - pref[u];
-    const int h = u % H, b = u / H;
-    const int cnt = unit_pages(seq_lens, sel, count, u, H, P);
-    const int npg = stage_chunk(cp, page_table, seq_lens, sel, u, c, cnt, H, P,
-                                max_pages);
-    lds_barrier();
-    if (u != cur_u) {
-      cur_u = u;
-      load_q_parts<D, G>(a, q, b, h, H, scale);
-    }
-    const int npos = npg * P;
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -INFINITY;
-      l[g] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
-    }
-    for (int gr0 = wave; gr0 < NGR; gr0 += 2 * kDecWaves) {
-      bf16x8_t kbv[2][KS];
-      Packed8<BF16> vv[2][NVI];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int base = 16 * (gr0 + e * kDecWaves);
-        {
-          const int i = base + n;
-          const int jj = i / P, t = i - jj * P;
-          const bool inb = i < npos;
-          const int slot = cp.slot[inb ? jj : 0];
-#pragma unroll
-          for (int s = 0; s < KS; ++s)
-            kbv[e][s] = inb ? *reinterpret_cast<const bf16x8_t *>(
-                                  kpool + pool_row(slot, h, t, H, P, D) + 32 * s + 8 * kb_of(lane))
-                            : bf16x8_t{};
-        }
-#pragma unroll
-        for (int vi = 0; vi < NVI; ++vi) {
-          const int i = base + vi * TPI + sub;
-          const int jj = i / P, t = i - jj * P;
-          if (i < npos)
-            vv[e][vi].load(vpool + pool_row(cp.slot[jj], h, t, H, P, D) + d0);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int base = 16 * (gr0 + e * kDecWaves);
-        const int i = base + n;
-        const int jj = i / P, t = i - jj * P;
-        const bool valid = lane < 16 && i < npos &&
-                           t < cp.nt[jj < kMaxChunkPages ? jj : 0];
-        float sv[G];
-#pragma unroll
-        for (int ps = 0; ps < NPASS; ++ps) {
-          f32x4_t cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s)
-            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ps][s], kbv[e][s], cc, 0, 0, 0);
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const float p1 = __shfl_down(cc[ii], 16, kWave);
-            const float p2 = __shfl_down(cc[ii], 32, kWave);
-            const int g = 4 * ps + ii;
-            if (g < G) sv[g] = valid ? cc[ii] + (p1 + p2) : -INFINITY;
-          }
-        }
-        float pv[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float gm = __shfl(group_max<16>(sv[g]), 0, kWave);
-          pv[g] = 0.f;
-          if (gm > -INFINITY) {  // the group holds a valid token
-            const float mn = fmaxf(m[g], gm);
-            const float sc = expf(m[g] - mn);  // 0 while m is -inf
-            pv[g] = expf(sv[g] - mn);          // 0 for invalid tokens
-            const float ps = __shfl(group_sum<16>(pv[g]), 0, kWave);
-            l[g] = fmaf(l[g], sc, ps);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[g][j] *= sc;
-            m[g] = mn;
-          }
-        }
-#pragma unroll
-        for (int vi = 0; vi < NVI; ++vi) {
-          const int tl = vi * TPI + sub;  // token within the group
-          const int i2 = base + tl;
-          const int jj2 = i2 / P, t2 = i2 - jj2 * P;
-          const bool ok = i2 < npos && t2 < cp.nt[jj2 < kMaxChunkPages ? jj2 : 0];
-          float xv[8];
-          vv[e][vi].unpack(xv);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float pw = __shfl(pv[g], tl, kWave);
-            if (ok) {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(pw, xv[j], acc[g][j]);
-            }
-          }
-        }
-      }
-    }
-    // merge the wave's token subgroups (lanes with equal li), then the waves
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = acc[g][j];
-#pragma unroll
-        for (int o = LPT; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-        acc[g][j] = v;
-      }
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) { s_m[wave][g] = m[g]; s_l[wave][g] = l[g]; }
-    }
-    if (sub == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s_acc[wave][g][d0 + j] = acc[g][j];
-    }
-    lds_barrier();
-    const size_t pc = static_cast<size_t>(u) * maxch + c;
-    for (int e = threadIdx.x; e < G * D; e += kDecThreads) {
-      const int g = e / D, d = e % D;
-      float M = s_m[0][g];
-#pragma unroll
-      for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, s_m[ww][g]);
-      float o = 0.f, ls = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kDecWaves; ++ww) {
-        const float wt = s_m[ww][g] > -INFINITY ? expf(s_m[ww][g] - M) : 0.f;
-        o = fmaf(wt, s_acc[ww][g][d], o);
-        ls = fmaf(wt, s_l[ww][g], ls);
-      }
-      part_o[pc * G * D + e] = o;
-      if (d == 0) {
-        part_l[pc * G + g] = ls;
-        part_m[pc * G + g] = M;
-      }
     }
     lds_barrier();
   }
@@ -1940,15 +1704,10 @@ hipError_t launch_softmax(const ekv_paged_kv &kv, const float *q, float scale,
   const int units = kv.batch * kv.num_kv_heads;
   const int blocks = persistent_blocks(static_cast<size_t>(units) * mc, 4);
   if constexpr (sizeof(typename E::T) == 2) {
-    hipLaunchKernelGGL((k_softmax_partial_mfma<D, G>), dim3(blocks),
-                       dim3(kDecThreads), 0, stream,
-                       static_cast<const uint16_t *>(kv.k),
-                       static_cast<const uint16_t *>(kv.v), kv.page_table,
-                       kv.seq_lens, sel, count, q, scale, units,
-                       kv.num_kv_heads, kv.page_size, kv.max_pages, mc,
-                       reinterpret_cast<float *>(w + L.part_m),
-                       reinterpret_cast<float *>(w + L.part_l),
-                       reinterpret_cast<float *>(w + L.part_o));
+    return launch_softmax_stream<D, G>(
+        kv, q, scale, sel, count, out, lse, reinterpret_cast<float *>(w + L.part_m),
+        reinterpret_cast<float *>(w + L.part_l), reinterpret_cast<float *>(w + L.part_o),
+        reinterpret_cast<int32_t *>(w + L.seg), stream);
   } else
   hipLaunchKernelGGL((k_softmax_partial<E, D, G>), dim3(blocks),
                      dim3(kDecThreads), 0, stream,

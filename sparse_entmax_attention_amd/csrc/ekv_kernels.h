@@ -53,8 +53,15 @@ struct DecodeWs {
 constexpr float kHintMargin = 0.03125f;
 DecodeWs decode_ws_layout(const ekv_paged_kv &kv);
 struct SoftmaxWs {
-  size_t part_m, part_l, part_o, total;
+  size_t part_m, part_l, part_o, seg, total;
 };
+size_t softmax_stream_slots(const ekv_paged_kv &kv);
+template <int D, int G>
+hipError_t launch_softmax_stream(const ekv_paged_kv &kv, const float *q,
+                                 float scale, const int32_t *sel,
+                                 const int32_t *count, float *out, float *lse,
+                                 float *part_m, float *part_l, float *part_o,
+                                 int32_t *seg_range, hipStream_t stream);
 SoftmaxWs softmax_ws_layout(const ekv_paged_kv &kv);
 
 template <class E, int D>

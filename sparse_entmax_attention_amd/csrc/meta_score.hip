@@ -129,9 +129,9 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
 //
 // One wave scores one tile of one (sequence, KV head) unit at a time: D/8
 // lanes per page (8 coordinates per lane, see coord_of), 64*8/D pages per
-// step.  The box bound uses max(q kmin, q kmax) = q+ kmax + q- kmin per
-// coordinate (q+ = max(q, 0), q- = min(q, 0)): the same rounded product is
-// picked either way.
+// step.  The box bound uses max(q kmin, q kmax) per coordinate, that is
+// q kmax where q > 0 and q kmin elsewhere (kmin <= kmax): one product per
+// coordinate, the larger of the two rounded ones.
 //
 // The metadata loads run kScoreRing steps ahead of the arithmetic: as soon
 // as a step's registers have been used they are refilled with the step
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
     load_q(nxt, qv);
 
     // this tile's query heads: scale * q at the lane's coordinates
-    float qs[G][8], qp[G][8], qn[G][8];
+    float qs[G][8], qb[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -500,8 +500,7 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
         if constexpr (kGauss) qs[g][j] = s_q[g * D + coord_of<float, D>(li, j)];
         if constexpr (kBox) {
           const float x = s_q[g * D + coord_of<T, D>(li, j)];
-          qp[g][j] = fmaxf(x, 0.f);
-          qn[g][j] = fminf(x, 0.f);
+          qb[g][j] = x;
         }
       }
     const size_t row0 = (static_cast<size_t>(cur.b) * Hq + cur.h * G) * max_pages;
@@ -525,8 +524,7 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
           float a = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            a = fmaf(qp[g][j], kmax[j], a);
-            a = fmaf(qn[g][j], kmin[j], a);
+            a = fmaf(qb[g][j], qb[g][j] > 0.f ? kmax[j] : kmin[j], a);
           }
           acc[g] = group_sum<LPP>(a);
         }
