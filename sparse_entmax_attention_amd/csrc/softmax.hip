@@ -242,10 +242,12 @@ __global__ __launch_bounds__(kDecThreads) void k_softmax_stream(
   }
 }
 
-// One block per (unit, query head) and kCombD coordinates: the unit's
-// segments merged in log-sum-exp form.
-constexpr int kSmCombD = 64;
-constexpr int kSmCombSlices = 4;
+// One block per (unit, query head) and kSmCombD coordinates: the unit's
+// segments merged in log-sum-exp form, kSmCombSlices threads per coordinate
+// taking every kSmCombSlices-th segment (a full cache has hundreds of
+// segments per unit).
+constexpr int kSmCombD = 16;
+constexpr int kSmCombSlices = 64;
 
 __global__ __launch_bounds__(kSmCombD * kSmCombSlices) void k_softmax_stream_combine(
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel,
