@@ -147,6 +147,40 @@ def test_cluster_1m_all_legs_sampled(gpu):
         assert abs(lse[b, h * G + j] - l) <= 1e-4 * max(1.0, abs(l))
 
 
+def test_cluster_1m_pages_of_16_full_cache_sampled(gpu):
+    """1M tokens in pages of 16: 524,288 page-heads, so every wave of the
+    full-cache key pass and of the streaming softmax walks some 170 pages,
+    several 64-page chunks of one unit (the query parts reloaded and the
+    page records written per chunk; the softmax segment carried across
+    chunks)."""
+    spec = workloads.workload("cluster_1m", page_size=16)
+    print("[case] cluster_1m, pages of 16, seed 3001", flush=True)
+    inp = workloads.generate(spec, 3001, gpu)
+    buf = ekv.DecodeBuffers(paged_kv(inp), softmax=True)
+    alpha = spec.alphas[0]
+    G, sc = spec.group, scale_of(spec)
+    buf.entmax(inp.q, alpha, selected=False)
+    torch.cuda.synchronize()
+    tau, out = f64(buf.tau), f64(buf.out)
+    b, h = 0, 3
+    print("[unit] full-cache entmax h=%d" % h, flush=True)
+    qs, keys, vals = unit_copy(inp, b, h)
+    for j in range(G):
+        o, t, _ = O.entmax_attend(qs[j], keys, vals, sc, alpha)
+        assert abs(tau[b, h * G + j] - t) <= TAU_ATOL, j
+        assert rel_l2(out[b, h * G + j], o) <= OUT_RTOL_L2, j
+    buf.softmax(inp.q)
+    torch.cuda.synchronize()
+    out, lse = f64(buf.out), f64(buf.lse)
+    b, h = 0, 4
+    print("[unit] full-cache softmax h=%d" % h, flush=True)
+    qs, keys, vals = unit_copy(inp, b, h)
+    for j in range(G):
+        o, l = O.softmax_attend(qs[j], keys, vals, sc)
+        assert rel_l2(out[b, h * G + j], o) <= OUT_RTOL_L2, j
+        assert abs(lse[b, h * G + j] - l) <= 1e-4 * max(1.0, abs(l)), j
+
+
 def test_ragged_pool_b16_appends_sampled(gpu):
     spec = workloads.workload("ragged_pool_b16")
     print("[case] ragged_pool_b16 full, seed 204, 3 appends", flush=True)
