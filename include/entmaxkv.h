@@ -341,9 +341,10 @@ ekv_status ekv_entmax_apply(const ekv_paged_kv *kv, float alpha,
 
 /*
  * ekv_softmax_decode - split-K softmax attention (the full-cache baseline
- * the Technical Summary, §4, compares against).  Each chunk of pages yields
- * (running max, sum of exponentials, weighted value sum); a second kernel
- * merges the chunks in log-sum-exp form.  sel/count as above (NULL sel =
+ * the Technical Summary, §4, compares against).  Each piece of the pages
+ * (bfloat16 K/V: a wave's run of pages within one unit; float32: a chunk of
+ * pages) yields (running max, sum of exponentials, weighted value sum); a
+ * second kernel merges the pieces in log-sum-exp form.  sel/count as above (NULL sel =
  * full cache).  out [batch][H_q][head_dim] float32; lse [batch][H_q]
  * float32 (natural log of sum_i exp(s_i)) or NULL.
  * Workspace: ekv_workspace_size(EKV_OP_SOFTMAX_DECODE, kv, 0).
