@@ -127,39 +127,46 @@ __global__ __launch_bounds__(kMetaThreads) void k_build_meta(
 //              max (mu + sqrt(2 ln P) sigma).
 // They live after the per-page values in the same buffers (see entmaxkv.h).
 //
-// One wave scores one tile of one (sequence, KV head) unit at a time: D/8
-// lanes per page (8 coordinates per lane, see coord_of), 64*8/D pages per
-// step.  The box bound uses max(q kmin, q kmax) per coordinate, that is
+// Two waves score one tile of one (sequence, KV head) unit at a time, each
+// half of its pages: D/8 lanes per page (8 coordinates per lane, see
+// coord_of), 64*8/D pages per step.  (Twice as many waves as tiles keep the
+// read stream fuller: with one wave per tile a 1M-token batch gives only two
+// waves per SIMD.)  The two waves of a tile sit in one block and merge their
+// halves' tile summaries through LDS; all waves of a block walk their items
+// in the same rounds, so every wave reaches every barrier.  The box bound uses max(q kmin, q kmax) per coordinate, that is
 // q kmax where q > 0 and q kmin elsewhere (kmin <= kmax): one product per
 // coordinate, the larger of the two rounded ones.
 //
 // The metadata loads run kScoreRing steps ahead of the arithmetic: as soon
 // as a step's registers have been used they are refilled with the step
-// kScoreRing further on, past the end of a tile with the first steps of the
-// wave's next tile, so each wave streams its records without a break.  Every
+// kScoreRing further on, past the end of a half tile with the first steps of
+// the wave's next one, so each wave streams its records without a break.  Every
 // load is unconditional (pages past a sequence's end re-read its last page),
 // which keeps the compiler's counts of loads in flight exact; a load behind a
 // branch would make it wait for all of them.  Tiles are numbered over those
 // that hold at least one page (a per-sequence prefix that every block builds
-// in LDS), KV head fastest, and dealt to the waves in turn: the waves running
-// together read every head's record of the same slots, one contiguous
-// stretch of the pool.  The query heads of a wave's next tile are staged
-// through the wave's own LDS rows while the current tile is scored.
+// in LDS), KV head fastest, and dealt to the wave pairs in turn: the waves
+// running together read every head's record of the same slots, one
+// contiguous stretch of the pool.  The query heads of a wave's next tile are
+// staged through the wave's own LDS rows while the current tile is scored.
 // ---------------------------------------------------------------------------
 constexpr int kScoreTile = kPageTile;
 constexpr int kScoreWaves = 4;
 constexpr int kScoreThreads = kScoreWaves * kWave;
-constexpr int kScoreRing = 4;
+constexpr int kScoreRing = 2;
+constexpr int kScorePairs = kScoreWaves / 2;
+constexpr int kScoreHalf = kPageTile / 2;  // pages per wave of a tile
 // Waves per SIMD the compiler is held to where that costs no spills: one
 // kind of record with up to four query heads per KV head (not float32 boxes
-// with four, whose 32-byte rows need more registers).  Elsewhere it may use
-// the whole register file.
+// with four, whose 32-byte rows need more registers); four for bfloat16
+// keys, three for float32 keys (whose tail-page rebuild holds a coordinate's
+// 64 values).  Elsewhere it may use the whole register file.
 template <class T, int G, int MODE>
 constexpr int score_min_waves() {
   if (MODE != EKV_SCORE_BBOX && MODE != EKV_SCORE_GAUSS) return 1;
   if (G > 4) return 1;
   if (G == 4 && MODE == EKV_SCORE_BBOX && sizeof(T) == 4) return 1;
-  return 3;
+  return sizeof(T) == 2 ? 4 : 3;
 }
 
 // The 8 coordinates of a row that a lane holds, as loaded (see coord_of).
@@ -337,15 +344,16 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   constexpr bool kGauss = (MODE & EKV_SCORE_GAUSS) != 0;
   constexpr int LPP = D / 8;               // lanes per page
   constexpr int PPS = kWave / LPP;         // pages per step
-  constexpr int NSTEP = kScoreTile / PPS;  // steps per tile
+  constexpr int NSTEP = kScoreHalf / PPS;  // steps per half tile
   constexpr int R = kScoreRing;
   constexpr int QF = G * D / kWave;        // staged query floats per lane
   static_assert(kScoreTile == kWave, "one page-table entry per lane");
-  static_assert(NSTEP >= R, "the ring must fit in a tile");
+  static_assert(NSTEP >= R, "the ring must fit in a half tile");
   static_assert(QF == 1 || QF == 2 || QF % 4 == 0, "query staging width");
   // the wave index (and everything derived from it) is wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int pair = wave >> 1, half = wave & 1;
   const int sub = lane / LPP, li = lane % LPP;
   const int Hq = H * G;
   const int n_tiles = (max_pages + kScoreTile - 1) / kScoreTile;
@@ -356,13 +364,21 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   // refreshing, the prefix of non-empty sequences (batch + 1 entries).  When
   // refreshing, the last tile of every non-empty sequence comes first in the
   // numbering (and the main prefix counts the other tiles), so that each is
-  // the first item of some wave (the host checks there are enough waves).
+  // the first item of some wave pair (the host checks there are enough pairs).
   extern __shared__ float4 s_dyn4[];
   float *s_q = reinterpret_cast<float *>(s_dyn4) + wave * G * D;
   int *s_pref = reinterpret_cast<int *>(s_dyn4) + kScoreWaves * G * D;
   int *s_np = s_pref + batch + 1;
   int *s_plast = s_np + batch;
   __shared__ int s_tmp[kScoreWaves];
+  // the second half's tile summaries, for the first half to merge (two
+  // buffers, alternating by round)
+  __shared__ float4 s_tg[2][kScorePairs][G];
+  __shared__ float s_tb[2][kScorePairs];
+  // a wave's (mu, sigma^2) of its half tile, [query head][page], written
+  // out in two coalesced stores at the half tile's end (a store per step,
+  // four scattered 32-byte pieces each, held up the record loads behind it)
+  __shared__ float2 s_gp[kScoreWaves][kGauss ? G * kScoreHalf : 1];
   {
     const int per = (batch + kScoreThreads - 1) / kScoreThreads;
     const int b0 = min(batch, threadIdx.x * per), b1 = min(batch, b0 + per);
@@ -396,9 +412,12 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   }
   const int n_last = REFRESH ? s_plast[batch] : 0;
   const int n_items = (s_pref[batch] + n_last) * H;
-  const int n_waves = gridDim.x * kScoreWaves;
-  int it = blockIdx.x * kScoreWaves + wave;
-  if (it >= n_items) return;  // whole waves; no block barrier follows
+  const int n_pairs = gridDim.x * kScorePairs;
+  // The block's items this round are itb .. itb + kScorePairs - 1; a pair
+  // whose item is past the end re-reads the last item and stores nothing.
+  int itb = blockIdx.x * kScorePairs;
+  if (itb >= n_items) return;  // the whole block
+  int it = itb + pair;
 
   // items only move forward, and so do their sequences in each part
   int blast = 0, bscan = 0;
@@ -420,13 +439,14 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
     }
     return d;
   };
-  // Slot of page (tile * 64 + lane), clamped to the sequence's last page.
+  // Slot of page (tile * 64 + lane), clamped to the sequence's last page
+  // (each wave loads the whole tile's and uses its half).
   auto load_slots = [&](const ScoreItem &d) {
     const int lp = min(d.tile * kScoreTile + lane, d.np - 1);
     return page_table[static_cast<size_t>(d.b) * max_pages + lp];
   };
   auto issue = [&](ScoreStep<T> &st, const ScoreItem &d, int slots, int t) {
-    const int slot = __shfl(slots, t * PPS + sub, kWave);
+    const int slot = __shfl(slots, half * kScoreHalf + t * PPS + sub, kWave);
     if constexpr (kBox) {
       const T *rb = bbox + meta_row(slot, d.h, 0, H, D);
       st.lo = load_raw8<D>(rb, li);
@@ -459,12 +479,15 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   };
 
   float qv[QF];
-  ScoreItem cur = describe(it);
-  if (REFRESH && it < n_last * H) {
-    // This wave's first tile is the last tile of its sequence: rebuild the
-    // metadata of the sequence's last page for this KV head before any of
-    // the tile's records is read.  The fence makes the wave's stores visible
-    // to its own later loads.
+  ScoreItem cur = describe(min(it, n_items - 1));
+  bool real = it < n_items;
+  if (REFRESH && real && it < n_last * H &&
+      half == ((cur.np - 1) % kScoreTile) / kScoreHalf) {
+    // This pair's first tile is the last tile of its sequence, and this
+    // wave's half holds the last page: rebuild that page's metadata for this
+    // KV head before any of the half's records is read (the other half never
+    // uses the page).  The fence makes the wave's stores visible to its own
+    // later loads.
     // (read by every lane from one address: uniform, kept in scalars)
     const int lp = cur.np - 1;
     const int slot = __builtin_amdgcn_readfirstlane(
@@ -484,10 +507,11 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
   float2 *gpage = reinterpret_cast<float2 *>(gstat);
   float4 *gtile = reinterpret_cast<float4 *>(gstat + gstat_tile_offset(batch, Hq, max_pages));
 
+  int par = 0;
   while (true) {
-    const int it_next = it + n_waves;
-    const bool more = it_next < n_items;
-    const ScoreItem nxt = more ? describe(it_next) : cur;
+    const int it_next = it + n_pairs;
+    const bool more = itb + n_pairs < n_items;  // the same for the block
+    const ScoreItem nxt = more ? describe(min(it_next, n_items - 1)) : cur;
     const int slots_next = load_slots(nxt);
     load_q(nxt, qv);
 
@@ -512,8 +536,8 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       ScoreStep<T> &st = ring[s % R];
-      const int lp = cur.tile * kScoreTile + s * PPS + sub;
-      const bool valid = lp < cur.np;
+      const int lp = cur.tile * kScoreTile + half * kScoreHalf + s * PPS + sub;
+      const bool valid = real && lp < cur.np;
       if constexpr (kBox) {
         float kmin[8], kmax[8];
         unpack8(st.lo, kmin);
@@ -567,32 +591,58 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
           pin(t_pr[g]);
           pin(t_kp[g]);
         }
-        if (valid && li < G) gpage[row0 + static_cast<size_t>(li) * max_pages + lp] = mine;
+        if (li < G) s_gp[wave][li * kScoreHalf + s * PPS + sub] = mine;
       }
-      // refill: the step R further on, in this tile or the wave's next one
-      // (none after its last tile)
+      // refill: the step R further on, in this half tile or the wave's next
+      // one (none after its last)
       if (s + R < NSTEP) issue(st, cur, slots_cur, s + R);
       else if (more) issue(st, nxt, slots_next, s + R - NSTEP);
     }
 
-    // tile summaries (every tile holds at least one valid page)
+    if constexpr (kGauss) {
+      const int base = cur.tile * kScoreTile + half * kScoreHalf;
+#pragma unroll
+      for (int e0 = 0; e0 < G * kScoreHalf; e0 += kWave) {
+        const int e = e0 + lane;
+        const int gg = e / kScoreHalf, pg = e % kScoreHalf;
+        if (e < G * kScoreHalf && real && base + pg < cur.np)
+          gpage[row0 + static_cast<size_t>(gg) * max_pages + base + pg] = s_gp[wave][e];
+      }
+    }
+    // Tile summaries: the second half's go through LDS to the first half,
+    // which writes the tile's (its first page is valid, so the first half
+    // holds at least one valid page; a half without one contributes
+    // -FLT_MAX).
+    float4 gsum = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (kBox) {
       tmax = cross_group_max<LPP>(tmax);
-      if (lane == 0)
-        ub[static_cast<size_t>(batch) * Hq * max_pages +
-           (static_cast<size_t>(cur.b) * H + cur.h) * n_tiles + cur.tile] = tmax;
+      if (half == 1 && lane == 0) s_tb[par][pair] = tmax;
     }
     if constexpr (kGauss) {
-      float4 mine = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float a0 = cross_group_max<LPP>(t_mu[g]);
         const float a1 = cross_group_max<LPP>(t_pr[g]);
         const float a2 = cross_group_max<LPP>(t_kp[g]);
-        if (lane == g) mine = make_float4(a0, a1, a2, 0.f);
+        if (lane == g) gsum = make_float4(a0, a1, a2, 0.f);
       }
-      if (lane < G)
-        gtile[(static_cast<size_t>(cur.b) * Hq + cur.h * G + lane) * n_tiles + cur.tile] = mine;
+      if (half == 1 && lane < G) s_tg[par][pair][lane] = gsum;
+    }
+    lds_barrier();
+    if (half == 0 && real) {
+      if constexpr (kBox) {
+        if (lane == 0)
+          ub[static_cast<size_t>(batch) * Hq * max_pages +
+             (static_cast<size_t>(cur.b) * H + cur.h) * n_tiles + cur.tile] =
+              fmaxf(tmax, s_tb[par][pair]);
+      }
+      if constexpr (kGauss) {
+        if (lane < G) {
+          const float4 o = s_tg[par][pair][lane];
+          gsum = make_float4(fmaxf(gsum.x, o.x), fmaxf(gsum.y, o.y), fmaxf(gsum.z, o.z), 0.f);
+          gtile[(static_cast<size_t>(cur.b) * Hq + cur.h * G + lane) * n_tiles + cur.tile] = gsum;
+        }
+      }
     }
     if (!more) break;
     // this tile's query reads are done (their values are in registers)
@@ -600,6 +650,9 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
     cur = nxt;
     slots_cur = slots_next;
     it = it_next;
+    itb += n_pairs;
+    real = it < n_items;
+    par ^= 1;
   }
 }
 
@@ -646,7 +699,7 @@ hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
             &per_cu, reinterpret_cast<const void *>(kern), kScoreThreads, lds) !=
             hipSuccess || per_cu <= 0)
       per_cu = 1;
-    const long long want = (items + kScoreWaves - 1) / kScoreWaves;
+    const long long want = (items + kScorePairs - 1) / kScorePairs;
     return static_cast<int>(
         std::min<long long>(want, static_cast<long long>(n_cu) * per_cu));
   };
@@ -659,12 +712,12 @@ hipError_t launch_score(const ekv_paged_kv &kv, const ekv_meta &meta,
                        meta.gauss);
     err = hipGetLastError();
   };
-  // the fused form needs a wave for every (sequence, KV head)
+  // the fused form needs a wave pair for every (sequence, KV head)
   auto run = [&](auto plain, auto fused) {
     if (refresh) {
       const int nb = grid_of(fused);
       if (static_cast<long long>(kv.batch) * kv.num_kv_heads <=
-          static_cast<long long>(nb) * kScoreWaves) {
+          static_cast<long long>(nb) * kScorePairs) {
         launch(fused, nb);
         return;
       }
