@@ -251,6 +251,61 @@ __device__ __forceinline__ void load_q_parts(bf16x8_t (&a)[(G + 3) / 4][D / 32],
   }
 }
 
+// The same operand as load_q_parts in two steps, for a kernel with LDS to
+// spare: load_q_rows issues the loads of the unit's G query rows, each
+// 16-byte piece once (lanes past the rows re-read the last one), and
+// q_parts_from_rows passes them through `stage`, the wave's own G*D/4
+// float4s of LDS, to the lanes that need them.  Every wave of a launch
+// starts by reading the same few KiB of queries; with the four lanes that
+// share a row each reading it (8 KiB per wave) that start waited several
+// microseconds on the caches.  Splitting the steps lets the caller issue
+// other loads between them.
+template <int D, int G>
+struct QRows {
+  static constexpr int kLoads = (G * D / 4 + kWave - 1) / kWave;  // per lane
+  float4 v[kLoads];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_q_rows(QRows<D, G> &r, const float *q, int b,
+                                            int h, int H) {
+  constexpr int NV = G * D / 4;  // float4s of the unit's rows
+  const int lane = threadIdx.x & (kWave - 1);
+  const float4 *src = reinterpret_cast<const float4 *>(
+      q + (static_cast<size_t>(b) * H * G + h * G) * D);
+#pragma unroll
+  for (int i = 0; i < QRows<D, G>::kLoads; ++i) r.v[i] = src[min(lane + kWave * i, NV - 1)];
+}
+
+template <int D, int G>
+__device__ __forceinline__ void q_parts_from_rows(bf16x8_t (&a)[(G + 3) / 4][D / 32],
+                                                  const QRows<D, G> &r, float zscale,
+                                                  float4 *stage) {
+  constexpr int NP = (G + 3) / 4, KS = D / 32;
+  constexpr int NV = G * D / 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, kb = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < QRows<D, G>::kLoads; ++i)
+    if (lane + kWave * i < NV) stage[lane + kWave * i] = r.v[i];
+  // (the wave's LDS operations complete in order: its reads below see the
+  // writes of all its lanes)
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int part = n >> 2, g = (n & 3) + 4 * ps;
+    const bool on = part < 3 && g < G;
+    const int row = (g < G ? g : 0) * (D / 4) + 2 * kb;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4 r0 = stage[row + 8 * s], r1 = stage[row + 8 * s + 1];
+      const float x[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        a[ps][s][i] = static_cast<__bf16>(on ? bf16_part(x[i] * zscale, part) : 0.f);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Grid sizing (host)
 // ---------------------------------------------------------------------------

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   __shared__ __align__(16) float s_z[kDecWaves][ZS];
   __shared__ float s_pm[kDecWaves][G][kWave];
   __shared__ unsigned long long s_mk[kDecWaves][G][kWave];
+  __shared__ float4 s_qs[kDecWaves][G * D / 4];  // the unit's queries, staged
   const int total = build_unit_prefix<kDecThreads>(pref, tmp, seq_lens, sel,
                                                    count, units, H, P, 1);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -121,25 +122,33 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
     // A chunk is up to 64 pages of one unit, so the unit's query parts and
     // score floors are loaded here, while no keys are in flight: loading
     // them inside the stream would hold their float32 sources in registers
-    // beside the ring, and the extra registers cost a wave per SIMD.
+    // beside the ring, and the extra registers cost a wave per SIMD.  The
+    // page references go first (the selection entries, then the page-table
+    // rows they name, are the chain to the first keys); the query rows and
+    // floors travel beside them and are turned into the matrix operand
+    // while the page-table rows are on their way.
     const int u = __builtin_amdgcn_readfirstlane(find_unit(pref, units, c0));
     const int c1 = min(min(c0 + kWave, f1), pref[u + 1]);
     const int nc = c1 - c0;                    // pages in this chunk
     const int nbc = (nc + U - 1) / U;          // bodies in this chunk
     const int h = u % H, b = u / H;
-    load_q_parts<D, G>(a, q, b, h, H, zscale);
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int g = 4 * ps + kb;
-      flo[ps] = g < G ? hint_floor(tau_hint, u * G + g) : -INFINITY;
-    }
     // page references, one page per lane (lanes past the chunk repeat its last)
     const int rj = c0 + min(lane, nc - 1) - pref[u];
     int rlp;
     if constexpr (SEL) rlp = sel[static_cast<size_t>(u) * max_pages + rj];
     else rlp = rj;
+    QRows<D, G> qrow;
+    load_q_rows<D, G>(qrow, q, b, h, H);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int g = 4 * ps + kb;
+      flo[ps] = g < G ? hint_floor(tau_hint, u * G + g) : -INFINITY;
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const int rnt = page_tokens(rlp, seq_lens[b], P);
     const int rslot = page_table[static_cast<size_t>(b) * max_pages + rlp];
+    __builtin_amdgcn_sched_barrier(0);
+    q_parts_from_rows<D, G>(a, qrow, zscale, s_qs[wave]);
     auto body_page = [&](int k, int t) { return min(k * U + t, nc - 1); };
 #pragma unroll
     for (int s = 0; s < kKRing; ++s) {
