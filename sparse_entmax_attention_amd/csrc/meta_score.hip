@@ -497,12 +497,15 @@ __global__ __launch_bounds__(kScoreThreads, (score_min_waves<typename E::T, G, M
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
+  // The first records are requested as soon as the page-table rows are in;
+  // the query rows, requested after those rows, are staged behind them.
   int slots_cur = load_slots(cur);
   load_q(cur, qv);
-  stage_q(qv);
   ScoreStep<T> ring[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) issue(ring[t], cur, slots_cur, t);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_q(qv);
   const float cP = sqrtf(2.0f * logf(static_cast<float>(P)));
   float2 *gpage = reinterpret_cast<float2 *>(gstat);
   float4 *gtile = reinterpret_cast<float4 *>(gstat + gstat_tile_offset(batch, Hq, max_pages));
