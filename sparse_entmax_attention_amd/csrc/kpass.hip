@@ -42,19 +42,34 @@ __device__ __forceinline__ float hint_floor(const float *tau_hint, int ug) {
   return t == t ? t - kHintMargin : -INFINITY;
 }
 
-// Block 0 records, for the threshold step, every head's score floor and its
-// query scaled by (alpha-1) scale (used to recompute scores when a hint
-// proves too high), and clears the count of heads left to the apply step.
+// Records, for the threshold step, every head's score floor and its query
+// scaled by (alpha-1) scale (used to recompute scores when a hint proves too
+// high), and clears the count of heads left to the apply step.  The heads are
+// spread over the grid, block b taking heads b, b + gridDim.x, ...: one
+// 16-byte load and store per lane and head.  (Block 0 alone, one float per
+// thread and round, made a chain of dependent round trips, 64 of them at
+// 128 heads, that held its own keys back by some 30 us.)  q and qz are
+// 16-byte aligned (checked at the entry points; qz sits in the workspace).
 template <int D>
 __device__ __forceinline__ void record_heads(const float *q, const float *tau_hint,
                                              float zscale, int n_heads,
                                              float *floor_ws, float *qz,
                                              int32_t *undone) {
-  if (blockIdx.x != 0) return;
-  if (threadIdx.x == 0) *undone = 0;
-  for (int i = threadIdx.x; i < n_heads; i += blockDim.x)
-    floor_ws[i] = hint_floor(tau_hint, i);
-  for (int i = threadIdx.x; i < n_heads * D; i += blockDim.x) qz[i] = q[i] * zscale;
+  constexpr int V = D / 4;  // float4s per head
+  static_assert(V < kDecThreads, "one lane per float4 of a head, one for the floor");
+  if (blockIdx.x == 0 && threadIdx.x == 0) *undone = 0;
+  for (int hd = blockIdx.x; hd < n_heads; hd += gridDim.x) {
+    if (threadIdx.x < V) {
+      float4 x = reinterpret_cast<const float4 *>(q)[static_cast<size_t>(hd) * V + threadIdx.x];
+      x.x *= zscale;
+      x.y *= zscale;
+      x.z *= zscale;
+      x.w *= zscale;
+      reinterpret_cast<float4 *>(qz)[static_cast<size_t>(hd) * V + threadIdx.x] = x;
+    } else if (threadIdx.x == V) {
+      floor_ws[hd] = hint_floor(tau_hint, hd);
+    }
+  }
 }
 
 template <int D, int G, int P, bool SEL>
