@@ -249,7 +249,11 @@ __device__ void recompute_head_scores(const typename E::T *kpool,
   __syncthreads();
 }
 
-template <class E, int D>
+// HALF: half the on-chip capacities (candidates and listed pages), about
+// 66 KiB of LDS instead of 128 KiB, so that two blocks share a CU; used when
+// there are more query heads than CUs (heads beyond the capacities take the
+// same overflow paths as in the full-size form).
+template <class E, int D, bool HALF>
 __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     float *__restrict__ zbuf, float *__restrict__ pmax,
     const typename E::T *__restrict__ vpool,
@@ -264,19 +268,21 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
     const float *__restrict__ floor_ws, const float *__restrict__ qz,
     const unsigned long long *__restrict__ pmask) {
   constexpr int NW = kTauThreads / kWave;
-  constexpr int SEGP = kTauPageCap / NW;  // listed pages per wave
-  constexpr int CSEG = kTauCandCap / NW;  // staged candidates per wave
+  constexpr int CandCap = HALF ? kTauCandCap / 2 : kTauCandCap;
+  constexpr int PageCap = HALF ? kTauPageCap / 2 : kTauPageCap;
+  constexpr int SEGP = PageCap / NW;  // listed pages per wave
+  constexpr int CSEG = CandCap / NW;  // staged candidates per wave
   __shared__ unsigned int hist[kTauBins];
   __shared__ int cpages[NW][SEGP];
-  __shared__ float cand[kTauCandCap];   // z of the staged candidates
-  __shared__ int cpos[kTauCandCap];     // their positions jj * P + t
+  __shared__ float cand[CandCap];   // z of the staged candidates
+  __shared__ int cpos[CandCap];     // their positions jj * P + t
   __shared__ float s_vacc[NW][D];
   __shared__ float s_vsum[NW];
   __shared__ float list[kTauList];
   __shared__ int s_nlist;
   __shared__ int s_npg[NW];
-  __shared__ int dense[kTauPageCap];   // listed pages (selection index j)
-  __shared__ int dslot[kTauPageCap];   // their pool slots
+  __shared__ int dense[PageCap];   // listed pages (selection index j)
+  __shared__ int dslot[PageCap];   // their pool slots
   __shared__ float s_wmax[NW];
   __shared__ int s_wscan[NW];
   __shared__ double s_wL[NW];
@@ -1028,7 +1034,7 @@ __global__ __launch_bounds__(kTauThreads) void k_entmax_tau(
   } else {
     // Steps of 4 kWave / P listed pages (4 scores per lane), dealt to the
     // waves in turn, US at a time; a step adds at most 4 kWave entries.
-    constexpr int US = 2;
+    constexpr int US = CSEG >= 2 * 2 * 4 * kWave ? 2 : 1;
     static_assert(CSEG >= 2 * US * 4 * kWave, "segment holds two passes");
     const int lpp = P / 4, ppw = kWave / lpp;
     const int sp = lane / lpp, t4 = 4 * (lane - sp * lpp);
@@ -1635,8 +1641,16 @@ hipError_t launch_entmax_threshold(const ekv_paged_kv &kv, float alpha,
   char *w = static_cast<char *>(ws);
   float rg;
   const int r = exponent_code(alpha, rg);
-  hipLaunchKernelGGL((k_entmax_tau<E, D>), dim3(kv.batch * kv.num_kv_heads * G),
-                     dim3(kTauThreads), 0, stream,
+  // one block per query head: with more heads than CUs the half-capacity
+  // form lets two blocks share a CU
+  const int n_heads = kv.batch * kv.num_kv_heads * G;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  auto kern = n_heads > n_cu ? k_entmax_tau<E, D, true> : k_entmax_tau<E, D, false>;
+  hipLaunchKernelGGL(kern, dim3(n_heads), dim3(kTauThreads), 0, stream,
                      reinterpret_cast<float *>(w + L.z),
                      reinterpret_cast<float *>(w + L.cmax),
                      static_cast<const typename E::T *>(kv.v),

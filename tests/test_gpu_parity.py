@@ -49,6 +49,12 @@ def inputs(name, device):
     return _cache[name]
 
 
+def heads_over_cus(heads_per_seq):
+    """Sequences enough for more query heads than the device has CUs."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return n_cu // heads_per_seq + 1
+
+
 def _units(inp):
     return [(b, h) for b in range(inp.spec.batch)
             for h in range(inp.spec.num_kv_heads)]
@@ -414,17 +420,21 @@ def test_topk_ties_across_tiles(gpu):
         assert list(buf.sel[0, h, :k].cpu().numpy()) == want
 
 
+@pytest.mark.parametrize("many", [False, True])
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
-def test_selection_with_candidates_beyond_lds(gpu, alpha):
+def test_selection_with_candidates_beyond_lds(gpu, alpha, many):
     # Keys of tiny magnitude put the scores of all 12,779 tokens within a few
     # thousandths of each other, inside the threshold bracket, so a head's
     # candidate scores do not fit on chip (8192 per head): with a selection the
     # threshold step walks the kept pages again to gather the support's
     # values, and the full cache leaves those heads to the apply step.  Both
-    # must match the oracle.
+    # must match the oracle.  With `many`, enough sequences share the same
+    # pages, query and length that there are more query heads than CUs (the
+    # threshold step's half-capacity form); every sequence must match.
     D, P, npg, H, G = 128, 64, 200, 2, 4
     n = npg * P - 21
-    print("[case] candidates beyond LDS, alpha %g" % alpha, flush=True)
+    B = heads_over_cus(H * G) if many else 1
+    print("[case] candidates beyond LDS, alpha %g, %d sequences" % (alpha, B), flush=True)
     g = torch.Generator(device="cpu")
     g.manual_seed(31)
     k = (3e-4 * torch.randn(npg, H, P, D, generator=g)).to(torch.bfloat16).to(gpu)
@@ -432,6 +442,7 @@ def test_selection_with_candidates_beyond_lds(gpu, alpha):
     pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
     sl = torch.tensor([n], dtype=torch.int32, device=gpu)
     q = torch.randn(1, H * G, D, generator=g).to(gpu)
+    pt, sl, q = pt.repeat(B, 1), sl.repeat(B), q.repeat(B, 1, 1)
     kv = ekv.PagedKV(k, v, pt, sl, G)
     buf = ekv.DecodeBuffers(kv)
     buf.build_meta()
@@ -458,20 +469,25 @@ def test_selection_with_candidates_beyond_lds(gpu, alpha):
             p = O.entmax_probs(z, t, alpha)
             o = (p[:, None] * vals).sum(0)
             for tau_, out_ in ((sel_tau, sel_out), (full_tau, full_out)):
-                assert abs(tau_[0, hq] - t) <= TAU_ATOL, (h, j)
-                assert rel_l2(out_[0, hq], o) <= OUT_RTOL_L2, (h, j)
+                for b in range(B):
+                    assert abs(tau_[b, hq] - t) <= TAU_ATOL, (b, h, j)
+                    assert rel_l2(out_[b, hq], o) <= OUT_RTOL_L2, (b, h, j)
 
 
+@pytest.mark.parametrize("many", [False, True])
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
-def test_threshold_with_pages_beyond_lds(gpu, alpha):
+def test_threshold_with_pages_beyond_lds(gpu, alpha, many):
     # 20,000 pages whose scores all lie within a few thousandths: more page
     # maxima than the threshold step holds in registers (16,384, the rest
     # are read again), more pages above its bracket than it lists on chip
     # (4,096) and more candidate scores than it stages (8,192).  Checked
-    # over the full cache and over a selection of every page.
+    # over the full cache and over a selection of every page; with `many`,
+    # as many sequences sharing those pages as make more query heads than
+    # CUs (the threshold step's half-capacity form).
     D, P, npg, G = 64, 16, 20000, 2
     n = npg * P - 7
-    print("[case] threshold with pages beyond LDS, alpha %g" % alpha, flush=True)
+    B = heads_over_cus(G) if many else 1
+    print("[case] threshold with pages beyond LDS, alpha %g, %d sequences" % (alpha, B), flush=True)
     g = torch.Generator(device="cpu")
     g.manual_seed(43)
     k = (3e-4 * torch.randn(npg, 1, P, D, generator=g)).to(gpu)
@@ -479,6 +495,7 @@ def test_threshold_with_pages_beyond_lds(gpu, alpha):
     pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
     sl = torch.tensor([n], dtype=torch.int32, device=gpu)
     q = torch.randn(1, G, D, generator=g).to(gpu)
+    pt, sl, q = pt.repeat(B, 1), sl.repeat(B), q.repeat(B, 1, 1)
     kv = ekv.PagedKV(k, v, pt, sl, G)
     buf = ekv.DecodeBuffers(kv)
     buf.build_meta()
@@ -504,8 +521,9 @@ def test_threshold_with_pages_beyond_lds(gpu, alpha):
         p = O.entmax_probs(z, t, alpha)
         o = (p[:, None] * vals).sum(0)
         for tau_, out_ in ((sel_tau, sel_out), (full_tau, full_out)):
-            assert abs(tau_[0, j] - t) <= TAU_ATOL, j
-            assert rel_l2(out_[0, j], o) <= OUT_RTOL_L2, j
+            for b in range(B):
+                assert abs(tau_[b, j] - t) <= TAU_ATOL, (b, j)
+                assert rel_l2(out_[b, j], o) <= OUT_RTOL_L2, (b, j)
 
 
 @pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (1.25, 0.0)])
