@@ -459,16 +459,22 @@ __device__ __forceinline__ void block_scan_multi(const int (&x)[L], int (&pre)[L
   }
 }
 
-template <int G, bool RULE>
-__global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
+// HALF: half the LDS capacities (about 65 KiB instead of 129 KiB), so that
+// two blocks share a CU (eight waves per SIMD); used when there are more
+// query heads than CUs.
+template <int G, bool RULE, bool HALF>
+__global__ __launch_bounds__(kGtThreads, HALF ? 8 : 1) void k_gauss_tau(
     const float *__restrict__ gstat, const int32_t *__restrict__ seq_lens,
     int batch, int H, int P, int max_pages, float am1, int r, float delta,
     float *__restrict__ tau_hat, unsigned long long *__restrict__ masks,
     const GaussRule rule) {
-  __shared__ float2 s_sv[kGtSvItems * kPageTile];  // (m, s); s < 0: last page
-  __shared__ float s_kz[kGtKzItems * kPageTile];
-  __shared__ int s_slist[kGtListCap];
-  __shared__ int s_klist[kGtListCap];
+  constexpr int SvItems = HALF ? kGtSvItems / 2 : kGtSvItems;
+  constexpr int KzItems = HALF ? kGtKzItems / 2 : kGtKzItems;
+  constexpr int ListCap = HALF ? kGtListCap / 2 : kGtListCap;
+  __shared__ float2 s_sv[SvItems * kPageTile];  // (m, s); s < 0: last page
+  __shared__ float s_kz[KzItems * kPageTile];
+  __shared__ int s_slist[ListCap];
+  __shared__ int s_klist[ListCap];
   __shared__ int s_scan[2 * kGtWaves];
   __shared__ float s_red[2][kGtWaves];
   __shared__ float2 s_fd[2][kGtWaves];
@@ -554,8 +560,8 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     cnt[1] += kf;
   }
   block_scan_multi<kGtThreads, 2>(cnt, pre, tot, s_scan);
-  const bool s_listed = tot[0] <= kGtListCap;
-  const bool k_listed = tot[1] <= kGtListCap;
+  const bool s_listed = tot[0] <= ListCap;
+  const bool k_listed = tot[1] <= ListCap;
   const int n_st = s_listed ? tot[0] : nt;  // otherwise every tile, in order
   const int n_kt = k_listed ? tot[1] : nt;
   for (int t = t_beg; t < t_end; ++t) {
@@ -588,7 +594,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
   // together (entries wave, wave + 8, ...).
   {
     constexpr int KS = 4, KK = 4;
-    const int s_lim = min(n_st, kGtSvItems), k_lim = min(n_kt, kGtKzItems);
+    const int s_lim = min(n_st, SvItems), k_lim = min(n_kt, KzItems);
     for (int c = 0;; ++c) {
       const int si0 = wave + c * KS * kGtWaves;
       const int ki0 = wave + c * KK * kGtWaves;
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     return next > t;
   };
   auto page_terms = [&](int i, float t, float &f, float &df) {
-    const float2 e = i < kGtSvItems ? s_sv[i * kPageTile + lane]
+    const float2 e = i < SvItems ? s_sv[i * kPageTile + lane]
                                     : surv_entry(surv_tile(i) * kPageTile + lane);
     if (e.x == -INFINITY) return;
     const bool last = e.y < 0.f;
@@ -659,7 +665,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     // below kGtDrop it is dropped for the remaining passes.  Together the
     // dropped terms stay under 16384 kGtDrop, far below float rounding of
     // F ~ 1.
-    if (i < kGtSvItems && tf < kGtDrop) s_sv[i * kPageTile + lane].x = -INFINITY;
+    if (i < SvItems && tf < kGtDrop) s_sv[i * kPageTile + lane].x = -INFINITY;
   };
   float tau = tau_lo, prev_step = INFINITY;
   for (int it = 0; it < 64; ++it) {
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(kGtThreads) void k_gauss_tau(
     const int t = keep_tile(k);
     const int p = t * kPageTile + lane;
     float z = -INFINITY;
-    if (k < kGtKzItems) z = s_kz[k * kPageTile + lane];
+    if (k < KzItems) z = s_kz[k * kPageTile + lane];
     else if (p < np) z = zhat(p, st[p]);
     const unsigned long long ball = __ballot(z > cut);
     if (lane == 0) mk[t] = ball;
@@ -836,7 +842,17 @@ hipError_t launch_select_gauss(const ekv_paged_kv &kv, const float *gstat,
   }
   const int units = kv.batch * kv.num_kv_heads;
   auto *masks = static_cast<unsigned long long *>(ws);
-  auto gt = r == 0 ? k_gauss_tau<G, true> : k_gauss_tau<G, false>;
+  // one block per query head: with more heads than CUs the half-capacity
+  // form lets two blocks share a CU (the closed forms only: the quadrature
+  // form does not fit eight waves per SIMD without spilling)
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  const bool half = units * G > n_cu;
+  auto gt = r == 0 ? k_gauss_tau<G, true, false>
+                   : (half ? k_gauss_tau<G, false, true> : k_gauss_tau<G, false, false>);
   hipLaunchKernelGGL(gt, dim3(units * G), dim3(kGtThreads), 0, stream, gstat,
                      kv.seq_lens, kv.batch, kv.num_kv_heads, kv.page_size,
                      kv.max_pages, alpha - 1.0f, r, delta, tau_hat, masks,

@@ -526,15 +526,19 @@ def test_threshold_with_pages_beyond_lds(gpu, alpha, many):
                 assert rel_l2(out_[b, j], o) <= OUT_RTOL_L2, (b, j)
 
 
+@pytest.mark.parametrize("many", [False, True])
 @pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (1.25, 0.0)])
-def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta):
+def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta, many):
     # Keys without structure give every page a score spread of about 1, so
     # no 64-page tile can be pruned: all 157 tiles survive and are keep
     # candidates, more than the selector holds on chip (128 of each), and
     # the rest are read from memory in the Newton passes and the keep test.
+    # With `many`, as many sequences sharing those pages as make more query
+    # heads than CUs (the selector's half-capacity form at alpha 1.5).
     D, P, npg, G = 64, 16, 10000, 2
     n = npg * P - 5
-    print("[case] Gaussian selector beyond LDS tiles, alpha %g" % alpha, flush=True)
+    B = heads_over_cus(G) if many else 1
+    print("[case] Gaussian selector beyond LDS tiles, alpha %g, %d sequences" % (alpha, B), flush=True)
     g = torch.Generator(device="cpu")
     g.manual_seed(41)
     k = torch.randn(npg, 1, P, D, generator=g).to(gpu)
@@ -542,6 +546,7 @@ def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta):
     pt = torch.randperm(npg, generator=g).to(torch.int32).reshape(1, npg).to(gpu)
     sl = torch.tensor([n], dtype=torch.int32, device=gpu)
     q = torch.randn(1, G, D, generator=g).to(gpu)
+    pt, sl, q = pt.repeat(B, 1), sl.repeat(B), q.repeat(B, 1, 1)
     kv = ekv.PagedKV(k, v, pt, sl, G)
     buf = ekv.DecodeBuffers(kv)
     buf.build_meta()
@@ -567,15 +572,19 @@ def test_gauss_selector_beyond_lds_tiles(gpu, alpha, delta):
     n_tl = (npg + 63) // 64
     assert n_tl > 128
     assert all(alive[:, 64 * t:64 * (t + 1)].any(axis=1).all() for t in range(n_tl))
-    for j in range(G):
-        assert abs(tau_hat[0, j] - th[j]) <= TAU_ATOL, j
+    for b in range(B):
+        for j in range(G):
+            assert abs(tau_hat[b, j] - th[j]) <= TAU_ATOL, (b, j)
     got = sel[0, 0, :cnt[0, 0]]
     assert cnt[0, 0] >= 1 and (np.diff(got) > 0).all()
     check_gauss_selection(got, mu, s2, n_tok, th, alpha, delta)
+    for b in range(1, B):  # the same inputs: the same selection
+        assert cnt[b, 0] == cnt[0, 0] and (sel[b, 0, :cnt[b, 0]] == got).all(), b
     ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
-    for j in range(G):
-        assert abs(tau[0, j] - ref["tau"][j]) <= TAU_ATOL, j
-        assert rel_l2(out[0, j], ref["out"][j]) <= OUT_RTOL_L2, j
+    for b in range(B):
+        for j in range(G):
+            assert abs(tau[b, j] - ref["tau"][j]) <= TAU_ATOL, (b, j)
+            assert rel_l2(out[b, j], ref["out"][j]) <= OUT_RTOL_L2, (b, j)
 
 
 @pytest.mark.parametrize("alpha", [1.25, 1.75, 1.1])
