@@ -108,8 +108,41 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   float *zst = s_z[wave];
   const int wg = blockIdx.x * kDecWaves + wave;
   const int per = ((total + U - 1) / U + nwaves - 1) / nwaves;  // bodies
-  const int f0 = wg * per * U;
-  const int f1 = min(total, f0 + per * U);
+  const int pw = per * U;                                        // pages per wave
+  int f0 = wg * pw;
+  int f1 = min(total, f0 + pw);
+  // A wave whose run crosses into another unit pays the whole start again
+  // (selection entries, page table, query rows) in the middle of the stream,
+  // and those waves ended last.  When the grid has waves enough, each unit
+  // gets its own ceil(pages / pw) waves instead, none crossing a unit
+  // boundary, no wave taking more than pw pages.  The waves-per-unit prefix
+  // lives in the query staging area, before any wave stages its queries
+  // (the same for the whole block, barriers included).
+  if (units < kDecWaves * G * D) {
+    int *wpref = reinterpret_cast<int *>(&s_qs[0][0]);
+    const int pt = (units + kDecThreads - 1) / kDecThreads;
+    const int u0 = min(units, static_cast<int>(threadIdx.x) * pt), u1 = min(units, u0 + pt);
+    auto waves_of = [&](int u) { return (pref[u + 1] - pref[u] + pw - 1) / pw; };
+    int local = 0;
+    for (int u = u0; u < u1; ++u) local += waves_of(u);
+    int need;
+    int base = block_excl_scan<kDecThreads>(local, tmp, need);
+    for (int u = u0; u < u1; ++u) {
+      wpref[u] = base;
+      base += waves_of(u);
+    }
+    lds_barrier();
+    if (need <= nwaves) {
+      if (wg < need) {
+        const int u = find_unit(wpref, units, wg);
+        f0 = pref[u] + (wg - wpref[u]) * pw;
+        f1 = min(pref[u + 1], f0 + pw);
+      } else {
+        f0 = f1 = total;
+      }
+    }
+    lds_barrier();  // every wave has read wpref
+  }
   if (f0 >= f1) return;  // whole waves; no block barrier follows
 
   // Keys of 16-token group t of page (slot, h) through a buffer resource on
