@@ -118,3 +118,72 @@ def test_random_shape_step(gpu, seed):
                 p = O.entmax_probs(z, t, alpha)
                 assert abs(f_tau[b, hq] - t) <= TAU_ATOL, (b, h, j)
                 assert rel_l2(f_out[b, hq], (p[:, None] * vals).sum(0)) <= OUT_RTOL_L2
+
+
+# Many small units: more units than the key pass's staging area holds for
+# its along-unit partition (G = 1, D = 64: 256), or more query heads than
+# CUs (the selector's and threshold step's half-capacity forms), with
+# sequences from one token up.
+MANY = [
+    dict(batch=300, num_kv_heads=1, group=1, head_dim=64, page_size=16, selector="gauss"),
+    dict(batch=40, num_kv_heads=4, group=2, head_dim=128, page_size=32, selector="topk"),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MANY)))
+def test_many_small_units(gpu, i):
+    m = dict(MANY[i])
+    selector = m.pop("selector")
+    alpha, delta, k = 1.5, 0.5, 6
+    spec = workloads.workload("ragged_pool_b16", kv_dtype="bf16", len_range=(1, 300),
+                              keys="clusters", needles=0, n_clusters=4,
+                              permute_slots=True, spare_pages=1, **m)
+    seed = 800 + i
+    print("[case] many small units seed=%d spec=%s selector=%s" % (seed, spec, selector),
+          flush=True)
+    inp = workloads.generate(spec, seed, gpu)
+    kv = paged_kv(inp)
+    buf = ekv.DecodeBuffers(kv)
+    buf.build_meta()
+    if selector == "gauss":
+        buf.score(inp.q, ekv.EKV_SCORE_GAUSS)
+        buf.select_gauss(alpha, delta)
+    else:
+        buf.score(inp.q, ekv.EKV_SCORE_BBOX)
+        buf.select_topk(k)
+    buf.entmax(inp.q, alpha)
+    torch.cuda.synchronize()
+    sel, cnt = buf.sel.cpu().numpy(), buf.count.cpu().numpy()
+    tau, out, tau_hat = f64(buf.tau), f64(buf.out), f64(buf.tau_hat)
+    buf.entmax(inp.q, alpha, selected=False)
+    torch.cuda.synchronize()
+    f_tau, f_out = f64(buf.tau), f64(buf.out)
+    host = HostCopy(inp)
+    P, G, sc = spec.page_size, spec.group, scale_of(spec)
+    for b in range(spec.batch):
+        for h in range(spec.num_kv_heads):
+            qs, keys, vals = host.unit(b, h)
+            n_tok = O.page_token_counts(keys.shape[0], P)
+            got = sel[b, h, :cnt[b, h]]
+            assert cnt[b, h] >= 1 and (np.diff(got) > 0).all(), (b, h)
+            if selector == "gauss":
+                _, _, mean, var = O.unit_metadata(keys, P)
+                mu, s2 = zip(*[O.gauss_moments(qs[j], mean, var, sc) for j in range(G)])
+                mu, s2 = np.stack(mu), np.stack(s2)
+                th = np.array([O.solve_tau_hat(mu[j], s2[j], n_tok, alpha) for j in range(G)])
+                for j in range(G):
+                    assert abs(tau_hat[b, h * G + j] - th[j]) <= TAU_ATOL, (b, h, j)
+                check_gauss_selection(got, mu, s2, n_tok, th, alpha, delta)
+            else:
+                want = O.decode_unit(qs, keys, vals, P, sc, alpha, "topk", k=k)
+                check_topk_selection(got, want, k)
+            ref = O.decode_unit(qs, keys, vals, P, sc, alpha, "given", pages=got)
+            for j in range(G):
+                hq = h * G + j
+                assert abs(tau[b, hq] - ref["tau"][j]) <= TAU_ATOL, (b, h, j)
+                assert rel_l2(out[b, hq], ref["out"][j]) <= OUT_RTOL_L2, (b, h, j)
+                z = (alpha - 1) * O.token_scores(qs[j], keys, sc)
+                t = O.entmax_threshold(z, alpha)
+                p = O.entmax_probs(z, t, alpha)
+                assert abs(f_tau[b, hq] - t) <= TAU_ATOL, (b, h, j)
+                assert rel_l2(f_out[b, hq], (p[:, None] * vals).sum(0)) <= OUT_RTOL_L2, (b, h, j)
