@@ -50,9 +50,6 @@ Pinning (see tests/test_oracle_*.py):
   * bf16_bits_to_f64, unit_tokens: pinned (exact decoding of known bit
     patterns; a scatter of numbered tokens through a random page table
     gathers back in order).
-  * round_bf16, stored_moments: pinned (hand-worked ties and roundings;
-    against the nearer of the two bfloat16 neighbours found from the
-    float32 bit pattern, ties to the even pattern).
   Planted mistakes in these functions (tests/oracle_mutants.py: dropped
   factors, wrong signs, roots, exponents, indices and tie rules) each fail
   at least one pin (tests/test_oracle_mutants.py).
@@ -72,8 +69,7 @@ from scipy import special as _sp
 
 __all__ = [
     "bf16_bits_to_f64", "unit_tokens", "page_token_counts", "page_metadata",
-    "unit_metadata", "round_bf16", "stored_moments", "token_scores",
-    "bbox_bound", "gauss_moments",
+    "unit_metadata", "token_scores", "bbox_bound", "gauss_moments",
     "group_bound", "select_topk", "excess_standard", "gauss_excess_moment",
     "gauss_normaliser", "solve_tau_hat",
     "page_max_estimate", "gauss_keep", "entmax_threshold",
@@ -148,31 +144,6 @@ def page_metadata(keys: np.ndarray):
     dev = keys - mean
     var = (dev * dev).sum(axis=0) / n
     return kmin, kmax, mean, var
-
-
-def round_bf16(x) -> np.ndarray:
-    """x rounded to the nearest bfloat16 (8 significant bits, ties to even).
-
-    A bfloat16 keeps 8 significant bits of the binary exponent form
-    x = m 2^e (0.5 <= |m| < 1): m 2^8 is rounded to the nearest integer, an
-    exact half to the even one, and scaled back.  (Values here are far from
-    the format's overflow and subnormal range.)
-    """
-    m, e = np.frexp(np.asarray(x, dtype=np.float64))
-    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
-
-
-def stored_moments(mean: np.ndarray, var: np.ndarray, kv_dtype: str):
-    """The page moments as a pool of kv_dtype stores them.
-
-    Reading: the pages leave the precision of the stored moments open; they
-    are kept in the KV cache's own dtype, as the box is (for bfloat16 keys
-    the box is exact, the moments are rounded to the nearest bfloat16).  For
-    float32 pools the moments are returned as computed here.
-    """
-    if kv_dtype == "bf16":
-        return round_bf16(mean), round_bf16(var)
-    return mean, var
 
 
 def unit_metadata(keys: np.ndarray, P: int):

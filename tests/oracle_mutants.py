@@ -201,17 +201,6 @@ def _group_bound_mean(ub):
     return np.asarray(ub, dtype=np.float64).mean(axis=0)
 
 
-def _round_bf16_truncate(x):
-    m, e = np.frexp(np.asarray(x, dtype=np.float64))
-    return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
-
-
-def _round_bf16_ties_away(x):
-    m, e = np.frexp(np.asarray(x, dtype=np.float64))
-    y = np.ldexp(m, 8)
-    return np.ldexp(np.sign(y) * np.floor(np.abs(y) + 0.5), e - 8)
-
-
 MUTANTS = {
     "entmax15_wrong_root": ("entmax_threshold", _entmax15_wrong_root),
     "sparsemax_extra_element": ("entmax_threshold", _sparsemax_extra_element),
@@ -241,8 +230,6 @@ MUTANTS = {
     "keep_first_head_only": ("gauss_keep", _keep_first_head_only),
     "group_bound_head0": ("group_bound", _group_bound_head0),
     "group_bound_mean": ("group_bound", _group_bound_mean),
-    "round_bf16_truncate": ("round_bf16", _round_bf16_truncate),
-    "round_bf16_ties_away": ("round_bf16", _round_bf16_ties_away),
 }
 
 
