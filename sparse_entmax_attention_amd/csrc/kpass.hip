@@ -117,8 +117,9 @@ __global__ __launch_bounds__(kDecThreads) void k_entmax_scores_mfma(
   // gets its own ceil(pages / pw) waves instead, none crossing a unit
   // boundary, no wave taking more than pw pages.  The waves-per-unit prefix
   // lives in the query staging area, before any wave stages its queries
-  // (the same for the whole block, barriers included).
-  if (units < kDecWaves * G * D) {
+  // (the same for the whole block, barriers included; skipped when there is
+  // nothing to do, pw = 0).
+  if (units < kDecWaves * G * D && pw > 0) {
     int *wpref = reinterpret_cast<int *>(&s_qs[0][0]);
     const int pt = (units + kDecThreads - 1) / kDecThreads;
     const int u0 = min(units, static_cast<int>(threadIdx.x) * pt), u1 = min(units, u0 + pt);
